@@ -1,0 +1,235 @@
+"""ctypes binding of libsx (include/sx.h).
+
+Argument marshalling only: every function here converts Python / torch
+arguments into the C ABI's plain pointers and sizes and calls the function of
+the same name in libsx.so.  Nothing is computed here.  If the library is not
+built this module raises on first use; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsx.so")
+
+SX_OK, SX_EINVAL, SX_EUNSUPPORTED, SX_EWORKSPACE, SX_EDEVICE = 0, -1, -2, -3, -4
+SX_F32, SX_BF16 = 0, 1
+SX_OP_REALIGN, SX_OP_RECOMPUTE, SX_OP_SELECT, SX_OP_TOPK, SX_OP_SPARSE_ATTN, SX_OP_FULL_ATTN = range(6)
+
+EXPORTED = [
+    "sx_rope_table", "sx_plan_layout", "sx_plan_realign", "sx_realign_jobs_bound",
+    "sx_workspace_bytes", "sx_rope_realign", "sx_recompute_kv", "sx_select_topk", "sx_topk",
+    "sx_sparse_attn", "sx_full_attn", "sx_last_error",
+]
+
+
+class SxError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class Dims(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("page_size", C.c_int32), ("dtype", C.c_int32)]
+
+
+class Pages(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("n_pages", C.c_int32)]
+
+
+class Layout(C.Structure):
+    _fields_ = [("n_req", C.c_int32), ("n_tok", C.c_int32), ("max_pages", C.c_int32),
+                ("rope_len", C.c_int32), ("seq_start", C.c_void_p), ("block_table", C.c_void_p),
+                ("pos_offset", C.c_void_p), ("rope_tab", C.c_void_p)]
+
+
+class RealignJob(C.Structure):
+    _fields_ = [("src_page", C.c_int32), ("dst_page", C.c_int32), ("src_slot", C.c_int32),
+                ("dst_slot", C.c_int32), ("n_tok", C.c_int32), ("delta", C.c_int32)]
+
+
+class Segment(C.Structure):
+    _fields_ = [("req", C.c_int32), ("dst_start", C.c_int32), ("len", C.c_int32),
+                ("p_src", C.c_int32), ("src_slot0", C.c_int32), ("src_pages_off", C.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libsx.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m segment_level_kv_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P, I, Z, D = C.c_void_p, C.c_int32, C.c_size_t, C.c_double
+        sig = {
+            "sx_rope_table": (I, [D, I, I, P]),
+            "sx_plan_layout": (I, [I, P, P, P, P, P, I, I, P, P, P, P, P, P]),
+            "sx_plan_realign": (I, [P, I, P, I, P, I, I, I, P, P, I, P]),
+            "sx_realign_jobs_bound": (I, [P, I, I]),
+            "sx_workspace_bytes": (Z, [I, P, I, I, I]),
+            "sx_rope_realign": (I, [P, P, P, P, P, I, P]),
+            "sx_recompute_kv": (I, [P, P, P, P, I, P, P, P, P]),
+            "sx_select_topk": (I, [P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, Z, P]),
+            "sx_topk": (I, [P, P, P, I, I, P, P, P, Z, P]),
+            "sx_sparse_attn": (I, [P, P, P, P, P, I, P, P, P, P, Z, P]),
+            "sx_full_attn": (I, [P, P, P, P, P, P, P, Z, P]),
+            "sx_last_error": (C.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().sx_last_error().decode()
+
+
+def _check(st: int, fn: str):
+    if st != SX_OK:
+        raise SxError(st, fn, last_error())
+
+
+def _ptr(t):
+    """Device/host address of a torch tensor or numpy array (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _ref(s):
+    return None if s is None else C.addressof(s)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# host planners
+# ---------------------------------------------------------------------------
+
+def sx_rope_table(theta: float, head_dim: int, n_pos: int) -> np.ndarray:
+    tab = np.empty((n_pos, head_dim // 2, 2), dtype=np.float32)
+    _check(lib().sx_rope_table(float(theta), head_dim, n_pos, _ptr(tab)), "sx_rope_table")
+    return tab
+
+
+def sx_plan_layout(requests, fallback_tokens: int = 64):
+    """requests: list of (pieces, (num, den)); pieces = [(is_reuse, length)].
+
+    Returns dict of numpy arrays: seq_start, tok_class, sq_rows, sq_start,
+    n_cand, k."""
+    n_req = len(requests)
+    piece_start = [0]
+    reuse, lens, num, den = [], [], [], []
+    for pieces, (a, b) in requests:
+        for is_reuse, L in pieces:
+            reuse.append(1 if is_reuse else 0)
+            lens.append(int(L))
+        piece_start.append(len(lens))
+        num.append(int(a))
+        den.append(int(b))
+    n_cap = max(1, sum(lens))
+    a32 = lambda v: np.ascontiguousarray(np.array(v, dtype=np.int32).reshape(-1))
+    ps, ru, ln, nu, de = a32(piece_start), a32(reuse or [0]), a32(lens or [0]), a32(num), a32(den)
+    seq_start = np.zeros(n_req + 1, np.int32)
+    tok_class = np.zeros(n_cap, np.uint8)
+    sq_rows = np.zeros(n_cap, np.int32)
+    sq_start = np.zeros(n_req + 1, np.int32)
+    n_cand = np.zeros(n_req, np.int32)
+    k = np.zeros(n_req, np.int32)
+    _check(lib().sx_plan_layout(n_req, _ptr(ps), _ptr(ru), _ptr(ln), _ptr(nu), _ptr(de),
+                                fallback_tokens, n_cap, _ptr(seq_start), _ptr(tok_class),
+                                _ptr(sq_rows), _ptr(sq_start), _ptr(n_cand), _ptr(k)),
+           "sx_plan_layout")
+    n_tok = int(seq_start[-1])
+    return dict(seq_start=seq_start, tok_class=tok_class[:n_tok], sq_rows=sq_rows[:sq_start[-1]],
+                sq_start=sq_start, n_cand=n_cand, k=k)
+
+
+def sx_plan_realign(segments, src_page_ids: np.ndarray, block_table: np.ndarray,
+                    pos_offset=None, page_size: int = 16) -> np.ndarray:
+    """segments: list of dict(req, dst_start, len, p_src, src_slot0,
+    src_pages_off).  Returns a structured int32 array [n_jobs, 6]."""
+    n = len(segments)
+    segs = (Segment * max(n, 1))()
+    for i, s in enumerate(segments):
+        segs[i] = Segment(s["req"], s["dst_start"], s["len"], s["p_src"], s.get("src_slot0", 0),
+                          s["src_pages_off"])
+    bound = lib().sx_realign_jobs_bound(segs, n, page_size)
+    jobs = np.zeros((max(bound, 1), 6), dtype=np.int32)
+    n_jobs = C.c_int32(0)
+    src = np.ascontiguousarray(src_page_ids, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    po = None if pos_offset is None else np.ascontiguousarray(pos_offset, dtype=np.int32)
+    _check(lib().sx_plan_realign(segs, n, _ptr(src), src.size, _ptr(bt), bt.shape[0], bt.shape[1],
+                                 page_size, _ptr(po), _ptr(jobs), jobs.shape[0], C.byref(n_jobs)),
+           "sx_plan_realign")
+    return jobs[:n_jobs.value].copy()
+
+
+def sx_workspace_bytes(op: int, dims: Dims, n_tok: int, n_rows: int, n_req: int) -> int:
+    return int(lib().sx_workspace_bytes(op, _ref(dims), n_tok, n_rows, n_req))
+
+
+# ---------------------------------------------------------------------------
+# device entry points (torch tensors in, nothing returned)
+# ---------------------------------------------------------------------------
+
+def sx_rope_realign(dims: Dims, lay: Layout, src: Pages, dst: Pages, jobs, n_jobs: int,
+                    stream=None):
+    _check(lib().sx_rope_realign(_ref(dims), _ref(lay), _ref(src), _ref(dst), _ptr(jobs), n_jobs,
+                                 _stream(stream)), "sx_rope_realign")
+
+
+def sx_recompute_kv(dims: Dims, lay: Layout, x, rows, n_rows: int, w_qkv, kv: Pages, q_out,
+                    stream=None):
+    _check(lib().sx_recompute_kv(_ref(dims), _ref(lay), _ptr(x), _ptr(rows), n_rows, _ptr(w_qkv),
+                                 _ref(kv), _ptr(q_out), _stream(stream)), "sx_recompute_kv")
+
+
+def sx_select_topk(dims: Dims, lay: Layout, q, q_index, sq_rows, sq_start, n_sq: int, lse,
+                   kv: Pages, tok_class, k_sel, sel_rows, act_rows, scores, ws, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sx_select_topk(_ref(dims), _ref(lay), _ptr(q), _ptr(q_index), _ptr(sq_rows),
+                                _ptr(sq_start), n_sq, _ptr(lse), _ref(kv), _ptr(tok_class),
+                                _ptr(k_sel), _ptr(sel_rows), _ptr(act_rows), _ptr(scores),
+                                _ptr(ws), ws_bytes, _stream(stream)), "sx_select_topk")
+
+
+def sx_topk(scores, tok_class, seq_start, n_req: int, n_tok: int, k_sel, sel_rows, ws,
+            stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sx_topk(_ptr(scores), _ptr(tok_class), _ptr(seq_start), n_req, n_tok, _ptr(k_sel),
+                         _ptr(sel_rows), _ptr(ws), ws_bytes, _stream(stream)), "sx_topk")
+
+
+def sx_sparse_attn(dims: Dims, lay: Layout, q, rows, row_start, n_rows: int, kv: Pages, o, lse,
+                   ws, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sx_sparse_attn(_ref(dims), _ref(lay), _ptr(q), _ptr(rows), _ptr(row_start),
+                                n_rows, _ref(kv), _ptr(o), _ptr(lse), _ptr(ws), ws_bytes,
+                                _stream(stream)), "sx_sparse_attn")
+
+
+def sx_full_attn(dims: Dims, lay: Layout, q, kv: Pages, o, lse, ws, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sx_full_attn(_ref(dims), _ref(lay), _ptr(q), _ref(kv), _ptr(o), _ptr(lse),
+                              _ptr(ws), ws_bytes, _stream(stream)), "sx_full_attn")

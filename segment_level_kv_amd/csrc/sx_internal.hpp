@@ -1,0 +1,65 @@
+// Host-side internal interface between the C ABI (api.cpp) and the kernel
+// launchers (*.hip).  Launchers assume validated arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sx.h"
+
+namespace sx {
+
+// Records `msg` as the calling thread's last error and returns `st`.
+sx_status set_error(sx_status st, const char* fmt, ...);
+// SX_OK, or SX_EDEVICE with the HIP error text if the last launch failed.
+sx_status check_launch(const char* what);
+
+// Lets `kernel` use `bytes` of dynamic LDS (gfx950 has 160 KB per CU).
+sx_status allow_lds(const void* kernel, size_t bytes, const char* what);
+
+// Attention query tile: 64 consecutive active rows of one request.
+constexpr int kTileRows = 64;
+struct AttnTile {
+  int32_t req;
+  int32_t row0;     // first row (index into the row list)
+  int32_t nrows;    // 1..kTileRows
+  int32_t pad;
+};
+
+// Workspace carving (all offsets 256-byte aligned).
+size_t align256(size_t x);
+size_t attn_ws_bytes(int n_rows, int n_req);
+size_t topk_ws_bytes(int n_tok, int n_req);
+size_t select_ws_bytes(const sx_dims& d, int n_tok, int n_sq, int n_req);
+
+sx_status launch_realign(const sx_dims& dims, const sx_layout& lay, const sx_pages& src,
+                         const sx_pages& dst, const sx_realign_job* jobs, int n_jobs,
+                         hipStream_t stream);
+
+sx_status launch_recompute(const sx_dims& dims, const sx_layout& lay, const void* x,
+                           const int32_t* rows, int n_rows, const void* w_qkv,
+                           const sx_pages& kv, void* q_out, hipStream_t stream);
+
+// Attention over the paged cache for rows grouped by request.
+//   rows == NULL: row m is packed token m (full prefill), row_start = seq_start.
+//   q_index (may be NULL): query of row m is q[q_index[m]].
+//   o == NULL: only the log-sum-exp is produced (probe pass).
+sx_status launch_attention(const sx_dims& dims, const sx_layout& lay, const void* q,
+                           const int32_t* q_index, const int32_t* rows,
+                           const int32_t* row_start, int n_rows, const sx_pages& kv, void* o,
+                           float* lse, void* ws, hipStream_t stream);
+
+// Per-(kv head, token) partial attention-mass scores of the Sparse-Q rows.
+sx_status launch_scores(const sx_dims& dims, const sx_layout& lay, const void* q,
+                        const int32_t* q_index, const int32_t* sq_rows, const int32_t* sq_start,
+                        int n_sq, const float* lse, const int32_t* lse_index,
+                        const sx_pages& kv, float* partial, hipStream_t stream);
+
+// Top-k on the sum over `n_parts` partial score rows ([n_parts][n_tok]).
+sx_status launch_topk(const float* partial, int n_parts, const uint8_t* tok_class,
+                      const int32_t* seq_start, int n_req, int n_tok, const int32_t* k_sel,
+                      const int32_t* sq_start, int32_t* sel_rows, int32_t* act_rows,
+                      float* scores_out, void* ws, hipStream_t stream);
+
+}  // namespace sx

@@ -1,0 +1,77 @@
+"""Helpers shared by the GPU parity tests (no method arithmetic here)."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+BF16_ULP_REL = 2.0 ** -8      # one bf16 rounding step is at most 2^-8 |x| (half of it: rounding)
+
+
+def say(*a):
+    """Print and flush before a GPU step so a failing run names its case."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_tol(ref: np.ndarray, atol: float = 1e-2) -> np.ndarray:
+    """bf16 storage tolerance: 1e-2 absolute plus one bf16 step of |ref|."""
+    return atol + BF16_ULP_REL * np.abs(ref)
+
+
+def assert_close_bf16(got, ref, atol=1e-2, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = np.abs(got - ref)
+    tol = bf16_tol(ref, atol)
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; "
+                           f"max err {err.max():.3g} at {np.unravel_index(err.argmax(), err.shape)}")
+    return float(err.max())
+
+
+def assert_close_f32(got, ref, rel=1e-4, what=""):
+    """fp32 storage: max |g - r| <= rel * max |r| per tensor."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    scale = max(np.max(np.abs(ref)), 1e-30)
+    err = np.max(np.abs(got - ref))
+    assert err <= rel * scale, f"{what}: max err {err:.3g} > {rel} * {scale:.3g}"
+    return float(err / scale)
+
+
+def bf16_ulps(a, b) -> np.ndarray:
+    """Distance in bf16 steps between two arrays of bf16-representable values."""
+    def key(x):
+        x = np.asarray(x, dtype=np.float32)
+        u = (x.view(np.uint32) >> 16).astype(np.int64)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return np.abs(key(a) - key(b))
+
+
+def selection_contract(gpu_sel, ora_scores, cand, k, tol):
+    """Top-k parity under floating-point scores: identical sets whenever the
+    oracle's k-th/(k+1)-th margin exceeds 2*tol; otherwise differences only
+    among candidates whose oracle score is within 2*tol of the k-th score.
+    Returns the number of differing indices."""
+    import oracle
+    ref = oracle.select_topk(ora_scores, cand, k)
+    got = np.sort(np.asarray(gpu_sel, dtype=np.int64))
+    assert len(got) == k and np.all(np.diff(got) > 0)
+    assert np.all(np.isin(got, cand))
+    if k == 0 or k == len(cand):
+        assert np.array_equal(got, ref)
+        return 0
+    s = np.sort(ora_scores[cand])[::-1]
+    kth, nxt = s[k - 1], s[k]
+    diff = np.setxor1d(got, ref)
+    if kth - nxt > 2 * tol:
+        assert len(diff) == 0, f"selection differs with margin {kth - nxt:.3g} > 2*tol {2 * tol:.3g}"
+    else:
+        near = np.abs(ora_scores[diff] - kth) <= 2 * tol
+        assert near.all(), "selection differs outside the near-tie band"
+    return len(diff)

@@ -1,0 +1,354 @@
+"""Per-kernel GPU parity against the CPU oracle on identical seeded inputs.
+
+Every entry point is called through the C ABI (libsx.so) and compared with
+the oracle function that defines the same step.  Tolerances:
+  fp32 storage: max |g - r| <= 1e-4 * max |r| per tensor;
+  bf16 storage: |g - r| <= 1e-2 + 2^-8 |r| per element (one bf16 rounding of
+  a value >= 4 alone exceeds 1e-2);
+  integer/index results and page-table writes: bit-exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from segment_level_kv_amd import _lib as L
+from segment_level_kv_amd import layer as LY
+from segment_level_kv_amd import synth
+from tests.gpu_util import (assert_close_bf16, assert_close_f32, bf16_ulps, say,
+                            selection_contract)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+SHAPES = {
+    "llama": synth.Dims(hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, theta=5e5, dtype="bf16"),
+    "qwen": synth.Dims(hidden=3584, n_q_heads=28, n_kv_heads=4, head_dim=128, theta=1e6, dtype="bf16"),
+    "tiny": synth.Dims(hidden=256, n_q_heads=4, n_kv_heads=1, head_dim=64, theta=1e4, dtype="f32"),
+}
+
+
+def _store(a, dims):
+    return synth.to_storage(a, dims.dtype)
+
+
+def _pool_from_logical(dims, n_pages, seed):
+    """Random page pool (values of the storage type) and its host copy."""
+    rng = np.random.default_rng(seed)
+    k = _store(rng.standard_normal((n_pages, dims.n_kv_heads, 16, dims.head_dim)), dims)
+    v = _store(rng.standard_normal((n_pages, dims.n_kv_heads, dims.head_dim, 16)), dims)
+    dt = LY.storage_dtype(dims.dtype)
+    pool = LY.PagePool(torch.from_numpy(k).to(dt).to(DEV), torch.from_numpy(v).to(dt).to(DEV))
+    return pool, k, v
+
+
+def _logical(kh, vh, page_ids, slot0, n):
+    """Host logical [n, Hkv, d] view of tokens slot0.. of a page list."""
+    ks, vs = [], []
+    for j in range(n):
+        p = page_ids[(slot0 + j) // 16]
+        s = (slot0 + j) % 16
+        ks.append(kh[p, :, s, :])
+        vs.append(vh[p, :, :, s])
+    return np.stack(ks), np.stack(vs)
+
+
+def _pool_host(pool):
+    return (pool.k.float().cpu().double().numpy(), pool.v.float().cpu().double().numpy())
+
+
+def _bits(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+
+
+# ------------------------------------------------------------------ realign --
+
+@pytest.mark.parametrize("shape", ["llama", "tiny"])
+def test_realign_parity_and_copy_semantics(shape):
+    dims = SHAPES[shape]
+    say(f"[realign] shape={shape}")
+    rng = np.random.default_rng(11)
+    n_pages = 96
+    pool, kh, vh = _pool_from_logical(dims, n_pages, 12)
+    perm = rng.permutation(n_pages).astype(np.int32)
+    # source pages 0..39 of perm, destination block table from 40..87, 88.. untouched
+    src_ids = perm[:40]
+    bt = perm[40:88].reshape(2, 24)
+    segs = [dict(req=0, dst_start=0, len=64, p_src=300, src_slot0=0, src_pages_off=0),
+            dict(req=0, dst_start=64, len=37, p_src=5, src_slot0=3, src_pages_off=4),
+            dict(req=0, dst_start=107, len=16, p_src=107, src_slot0=0, src_pages_off=8),   # delta 0
+            dict(req=1, dst_start=5, len=200, p_src=9000, src_slot0=11, src_pages_off=10),
+            dict(req=1, dst_start=230, len=20, p_src=0, src_slot0=0, src_pages_off=30)]
+    pos_off = np.array([0, 1234], np.int32)
+    jobs = L.sx_plan_realign(segs, src_ids, bt, pos_offset=pos_off)
+    rope = LY.rope_table(dims.theta, dims.head_dim, 12000, DEV)
+    lay = LY.DeviceLayout(np.array([0, 256, 512], np.int32), bt, rope, DEV, pos_offset=pos_off)
+    before_k, before_v = _bits(pool.k), _bits(pool.v)
+    jt = torch.from_numpy(jobs).to(DEV)
+    L.sx_rope_realign(LY.make_dims(dims), lay.struct, pool.struct(), pool.struct(), jt, len(jobs))
+    torch.cuda.synchronize()
+    ak, av = _pool_host(pool)
+    after_k, after_v = _bits(pool.k), _bits(pool.v)
+    written = np.zeros((n_pages, 16), dtype=bool)
+    for s in segs:
+        kc, vc = _logical(kh, vh, src_ids[s["src_pages_off"]:], s["src_slot0"], s["len"])
+        p_dst = s["dst_start"] + pos_off[s["req"]]
+        kr, vr = oracle.realign_segment(kc, vc, s["p_src"], p_dst, dims.theta, dims.dtype)
+        kg, vg = _logical(ak, av, bt[s["req"]], s["dst_start"], s["len"])
+        assert np.array_equal(vg, vr), "V must be copied bit-exactly"
+        if p_dst == s["p_src"]:
+            assert np.array_equal(kg, kr), "delta 0 must copy K bit-exactly"
+        if dims.dtype == "bf16":
+            assert bf16_ulps(kg, kr).max() <= 1
+            assert_close_bf16(kg, kr, what="realigned K")
+        else:
+            assert_close_f32(kg, kr, what="realigned K")
+        for j in range(s["len"]):
+            t = s["dst_start"] + j
+            written[bt[s["req"], t // 16], t % 16] = True
+    # sources and every slot no segment maps to are bit-unchanged
+    for p in range(n_pages):
+        for sl in range(16):
+            if not written[p, sl]:
+                assert np.array_equal(after_k[p, :, sl], before_k[p, :, sl])
+                assert np.array_equal(after_v[p, :, :, sl], before_v[p, :, :, sl])
+
+
+# ---------------------------------------------------------------- recompute --
+
+@pytest.mark.parametrize("shape,n_rows", [("llama", 300), ("qwen", 130), ("tiny", 40)])
+def test_recompute_parity_and_scatter(shape, n_rows):
+    dims = SHAPES[shape]
+    say(f"[recompute] shape={shape} rows={n_rows}")
+    rng = np.random.default_rng(21)
+    seq = np.array([0, 700, 1000], np.int32)
+    n_tok = int(seq[-1])
+    x = _store(synth._rmsnormed_gaussian(rng, n_tok, dims.hidden, dims.eps), dims)
+    case_w = synth._weights(rng, dims)
+    w = np.concatenate(case_w, axis=0)
+    rows = np.sort(rng.choice(n_tok, size=n_rows, replace=False)).astype(np.int32)
+    rng.shuffle(rows)                             # row order need not be sorted
+    n_pages = 80
+    pool = LY.PagePool.alloc(n_pages, dims, DEV)
+    perm = rng.permutation(n_pages).astype(np.int32)
+    bt = perm[:2 * 44].reshape(2, 44)
+    rope = LY.rope_table(dims.theta, dims.head_dim, 1100, DEV)
+    pos_off = np.array([0, 77], np.int32)
+    lay = LY.DeviceLayout(seq, bt, rope, DEV, pos_offset=pos_off)
+    dt = LY.storage_dtype(dims.dtype)
+    xt = torch.from_numpy(x).to(dt).to(DEV)
+    wt = torch.from_numpy(w).to(dt).to(DEV)
+    rt = torch.from_numpy(rows).to(DEV)
+    q = torch.full((n_rows, dims.n_q_heads, dims.head_dim), 7.0, dtype=dt, device=DEV)
+    before_k, before_v = _bits(pool.k), _bits(pool.v)
+    L.sx_recompute_kv(LY.make_dims(dims), lay.struct, xt, rt, n_rows, wt, pool.struct(), q)
+    torch.cuda.synchronize()
+    req = (rows >= 700).astype(int)
+    idx = rows - seq[req]
+    pos = idx + pos_off[req]
+    qr, kr, vr = oracle.project_rows(x[rows], case_w[0], case_w[1], case_w[2], pos, dims.theta,
+                                     dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.dtype)
+    qg = q.float().cpu().double().numpy()
+    ak, av = _pool_host(pool)
+    kg = np.stack([ak[bt[r, i // 16], :, i % 16, :] for r, i in zip(req, idx)])
+    vg = np.stack([av[bt[r, i // 16], :, :, i % 16] for r, i in zip(req, idx)])
+    if dims.dtype == "bf16":
+        for g_, r_, nm in [(qg, qr, "Q"), (kg, kr, "K"), (vg, vr, "V")]:
+            assert bf16_ulps(g_, r_).max() <= 1, nm
+            assert_close_bf16(g_, r_, what=nm)
+    else:
+        assert_close_f32(qg, qr, what="Q")
+        assert_close_f32(kg, kr, what="K")
+        assert_close_f32(vg, vr, what="V")
+    # exactly the listed rows' slots were written
+    after_k, after_v = _bits(pool.k), _bits(pool.v)
+    hit = np.zeros((n_pages, 16), dtype=bool)
+    for r, i in zip(req, idx):
+        hit[bt[r, i // 16], i % 16] = True
+    for p in range(n_pages):
+        for sl in range(16):
+            if not hit[p, sl]:
+                assert np.array_equal(after_k[p, :, sl], before_k[p, :, sl])
+                assert np.array_equal(after_v[p, :, :, sl], before_v[p, :, :, sl])
+
+
+# ---------------------------------------------------------------- attention --
+
+def _attn_inputs(dims, lens, seed):
+    rng = np.random.default_rng(seed)
+    seq = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    req_pages = [(n + 15) // 16 for n in lens]
+    n_pages = sum(req_pages) + 4
+    pool, kh, vh = _pool_from_logical(dims, n_pages, seed + 1)
+    perm = rng.permutation(n_pages).astype(np.int32)
+    bt = np.full((len(lens), max(req_pages)), -1, np.int32)
+    o = 0
+    for r, n in enumerate(req_pages):
+        bt[r, :n] = perm[o:o + n]
+        o += n
+    return rng, seq, pool, kh, vh, bt
+
+
+@pytest.mark.parametrize("shape,lens,density,qscale", [
+    ("llama", [700, 333], 0.3, 1.0),
+    ("llama", [1500], 0.12, 3.0),
+    ("qwen", [650, 90], 0.4, 2.0),
+    ("tiny", [144, 50], 0.5, 1.0),
+])
+def test_sparse_attention_parity(shape, lens, density, qscale):
+    dims = SHAPES[shape]
+    say(f"[attn] shape={shape} lens={lens} density={density}")
+    rng, seq, pool, kh, vh, bt = _attn_inputs(dims, lens, 31)
+    rows, starts = [], [0]
+    for r, n in enumerate(lens):
+        sel = np.flatnonzero(rng.random(n) < density)
+        sel = np.union1d(sel, [0, n - 1])                      # first and last token included
+        rows.append(sel + seq[r])
+        starts.append(starts[-1] + len(sel))
+    rows = np.concatenate(rows).astype(np.int32)
+    n_rows = len(rows)
+    q = _store(rng.standard_normal((n_rows, dims.n_q_heads, dims.head_dim)) * qscale, dims)
+    dt = LY.storage_dtype(dims.dtype)
+    rope = LY.rope_table(dims.theta, dims.head_dim, 16, DEV)
+    lay = LY.DeviceLayout(seq, bt, rope, DEV)
+    cd = LY.make_dims(dims)
+    o = torch.zeros((n_rows, dims.n_q_heads * dims.head_dim), dtype=dt, device=DEV)
+    lse = torch.zeros((n_rows, dims.n_q_heads), dtype=torch.float32, device=DEV)
+    ws = LY.workspace(L.SX_OP_SPARSE_ATTN, cd, int(seq[-1]), n_rows, len(lens), DEV)
+    L.sx_sparse_attn(cd, lay.struct, torch.from_numpy(q).to(dt).to(DEV), torch.from_numpy(rows).to(DEV),
+                     torch.from_numpy(np.array(starts, np.int32)).to(DEV), n_rows, pool.struct(), o, lse, ws)
+    torch.cuda.synchronize()
+    og = o.float().cpu().double().numpy()
+    lg = lse.cpu().double().numpy()
+    for r in range(len(lens)):
+        K, V = _logical(kh, vh, bt[r], 0, lens[r])
+        sl = slice(starts[r], starts[r + 1])
+        ref, lref = oracle.causal_attention(q[sl], rows[sl] - seq[r], K, V)
+        ref = ref.reshape(len(ref), -1)
+        if dims.dtype == "bf16":
+            assert_close_bf16(og[sl], ref, what=f"O req {r}")
+            assert np.max(np.abs(lg[sl] - lref)) < 2e-3
+        else:
+            assert_close_f32(og[sl], ref, what=f"O req {r}")
+            assert np.max(np.abs(lg[sl] - lref)) < 1e-4
+
+
+@pytest.mark.parametrize("shape,lens", [("llama", [900, 130]), ("tiny", [144])])
+def test_full_attention_parity(shape, lens):
+    dims = SHAPES[shape]
+    say(f"[full attn] shape={shape} lens={lens}")
+    rng, seq, pool, kh, vh, bt = _attn_inputs(dims, lens, 41)
+    n_tok = int(seq[-1])
+    q = _store(rng.standard_normal((n_tok, dims.n_q_heads, dims.head_dim)), dims)
+    dt = LY.storage_dtype(dims.dtype)
+    lay = LY.DeviceLayout(seq, bt, LY.rope_table(dims.theta, dims.head_dim, 16, DEV), DEV)
+    cd = LY.make_dims(dims)
+    o = torch.zeros((n_tok, dims.n_q_heads * dims.head_dim), dtype=dt, device=DEV)
+    ws = LY.workspace(L.SX_OP_FULL_ATTN, cd, n_tok, n_tok, len(lens), DEV)
+    L.sx_full_attn(cd, lay.struct, torch.from_numpy(q).to(dt).to(DEV), pool.struct(), o, None, ws)
+    torch.cuda.synchronize()
+    og = o.float().cpu().double().numpy()
+    for r in range(len(lens)):
+        K, V = _logical(kh, vh, bt[r], 0, lens[r])
+        sl = slice(seq[r], seq[r + 1])
+        ref, _ = oracle.causal_attention(q[sl], np.arange(lens[r]), K, V)
+        ref = ref.reshape(len(ref), -1)
+        if dims.dtype == "bf16":
+            assert_close_bf16(og[sl], ref, what=f"O req {r}")
+        else:
+            assert_close_f32(og[sl], ref, what=f"O req {r}")
+
+
+# ------------------------------------------------------------ probe + top-k --
+
+@pytest.mark.parametrize("shape,lens,n_new", [("llama", [1200, 500], 70), ("qwen", [800], 40),
+                                              ("tiny", [144, 60], 16)])
+def test_select_topk_parity(shape, lens, n_new):
+    dims = SHAPES[shape]
+    say(f"[select] shape={shape} lens={lens}")
+    rng, seq, pool, kh, vh, bt = _attn_inputs(dims, lens, 51)
+    n_tok = int(seq[-1])
+    tok_class = np.zeros(n_tok, np.uint8)
+    sq_rows, sq_start, ks = [], [0], []
+    for r, n in enumerate(lens):
+        sq = np.union1d(np.arange(n - n_new, n), rng.choice(n, size=n_new // 4, replace=False))
+        tok_class[sq + seq[r]] = 1
+        sq_rows.append(sq + seq[r])
+        sq_start.append(sq_start[-1] + len(sq))
+        ks.append(int(0.2 * (n - len(sq))))
+    sq_rows = np.concatenate(sq_rows).astype(np.int32)
+    n_sq = len(sq_rows)
+    q = _store(rng.standard_normal((n_sq, dims.n_q_heads, dims.head_dim)) * 2.0, dims)
+    dt = LY.storage_dtype(dims.dtype)
+    lay = LY.DeviceLayout(seq, bt, LY.rope_table(dims.theta, dims.head_dim, 16, DEV), DEV)
+    cd = LY.make_dims(dims)
+    k_sel = np.array(ks, np.int32)
+    sel = torch.full((int(k_sel.sum()),), -7, dtype=torch.int32, device=DEV)
+    act = torch.full((n_sq + int(k_sel.sum()),), -7, dtype=torch.int32, device=DEV)
+    scores = torch.zeros(n_tok, dtype=torch.float32, device=DEV)
+    ws = LY.workspace(L.SX_OP_SELECT, cd, n_tok, n_sq, len(lens), DEV)
+    L.sx_select_topk(cd, lay.struct, torch.from_numpy(q).to(dt).to(DEV), None,
+                     torch.from_numpy(sq_rows).to(DEV), torch.from_numpy(np.array(sq_start, np.int32)).to(DEV),
+                     n_sq, None, pool.struct(), torch.from_numpy(tok_class).to(DEV),
+                     torch.from_numpy(k_sel).to(DEV), sel, act, scores, ws)
+    torch.cuda.synchronize()
+    sg = scores.cpu().double().numpy()
+    selg = sel.cpu().numpy()
+    actg = act.cpu().numpy()
+    off = 0
+    for r, n in enumerate(lens):
+        K, _ = _logical(kh, vh, bt[r], 0, n)
+        sl = slice(sq_start[r], sq_start[r + 1])
+        qpos = sq_rows[sl] - seq[r]
+        _, lse = oracle.causal_attention(q[sl], qpos, K, K)
+        ref = oracle.attention_mass_scores(q[sl], qpos, K, lse)
+        got = sg[seq[r]:seq[r + 1]]
+        tol = 2e-5 * ref.max()
+        err = np.abs(got - ref)
+        assert np.all(err <= 1e-4 * ref + tol), f"scores: max rel err {np.max(err / (ref + tol)):.3g}"
+        cand = np.flatnonzero(tok_class[seq[r]:seq[r + 1]] == 0)
+        gsel = selg[off:off + ks[r]] - seq[r]
+        assert np.all(np.diff(gsel) > 0), "selection must be ascending"
+        ndiff = selection_contract(gsel, ref, cand, ks[r], tol + 1e-4 * ref.max())
+        # active set = Sparse-Q rows merged with the selection, ascending
+        a_off = sq_start[r] + off
+        ga = actg[a_off:a_off + len(qpos) + ks[r]] - seq[r]
+        assert np.array_equal(ga, np.union1d(qpos, gsel))
+        say(f"  req {r}: k={ks[r]} differing indices={ndiff}")
+        off += ks[r]
+
+
+def test_topk_bit_exact_adversarial():
+    """Top-k on identical scores must equal the oracle bit for bit,
+    including all-equal scores, two-valued scores and signed zeros."""
+    say("[topk] adversarial")
+    rng = np.random.default_rng(61)
+    lens = [3000, 1, 700, 5000, 2048, 100]
+    seq = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    n_tok = int(seq[-1])
+    parts = [rng.standard_normal(3000).astype(np.float32), np.zeros(1, np.float32),
+             np.full(700, 0.5, np.float32),
+             np.where(rng.random(5000) < 0.5, 2.0, 1.0).astype(np.float32),
+             np.where(rng.random(2048) < 0.5, 0.0, -0.0).astype(np.float32),
+             (np.round(rng.random(100) * 3) / 4).astype(np.float32)]
+    scores = np.concatenate(parts)
+    tok_class = (rng.random(n_tok) < 0.2).astype(np.uint8)
+    ks = [1000, 1, 333, 2500, 900, 0]
+    n_cand = [int(np.sum(tok_class[seq[r]:seq[r + 1]] == 0)) for r in range(len(lens))]
+    ks = [min(k, c) for k, c in zip(ks, n_cand)]
+    sel = torch.full((sum(ks),), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(L.sx_workspace_bytes(L.SX_OP_TOPK, LY.make_dims(SHAPES["llama"]), n_tok, 0, len(lens)),
+                     dtype=torch.uint8, device=DEV)
+    L.sx_topk(torch.from_numpy(scores).to(DEV), torch.from_numpy(tok_class).to(DEV),
+              torch.from_numpy(seq).to(DEV), len(lens), n_tok, torch.from_numpy(np.array(ks, np.int32)).to(DEV),
+              sel, ws)
+    torch.cuda.synchronize()
+    got = sel.cpu().numpy()
+    off = 0
+    for r in range(len(lens)):
+        sc = scores[seq[r]:seq[r + 1]].astype(np.float64)
+        cand = np.flatnonzero(tok_class[seq[r]:seq[r + 1]] == 0)
+        ref = oracle.select_topk(sc, cand, ks[r])
+        assert np.array_equal(got[off:off + ks[r]] - seq[r], ref), f"request {r}"
+        off += ks[r]

@@ -1,0 +1,123 @@
+"""End-to-end GPU parity of one SparseX layer against the CPU oracle.
+
+Both sides start from the same seeded inputs (layer input rows, weights,
+segment layout and original offsets) and each builds its own segment caches,
+realigns them, probes, selects, recomputes and attends.  Compared:
+  - the selected set S: bit-exact whenever the oracle's k-th/(k+1)-th score
+    margin exceeds twice the score tolerance, else differing only inside that
+    near-tie band (reported);
+  - the final mixed K/V cache of every token, the scores and the layer output
+    O of every active row, within the storage tolerances;
+  - the page-table writes: pages outside the batch (guard pages) unchanged.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from segment_level_kv_amd import synth
+from segment_level_kv_amd.layer import SparseXLayerRun
+from tests.gpu_util import assert_close_bf16, assert_close_f32, say, selection_contract
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_request(case, r, ratio):
+    d = case.dims
+    plan = oracle.plan_request(case.piece_lengths(r), ratio)
+    segs = []
+    for dst, sid in case.reuse_runs(r):
+        sg = case.segments[sid]
+        pos = np.arange(sg.length) + sg.p_src
+        _, k, v = oracle.project_rows(sg.x_cache, case.wq, case.wk, case.wv, pos, d.theta,
+                                      d.n_q_heads, d.n_kv_heads, d.head_dim, d.dtype, want_q=False)
+        segs.append((dst, sg.p_src, k, v))
+    out = oracle.sparse_layer(case.request_x(r), case.wq, case.wk, case.wv, plan, segs, d.theta,
+                              d.n_q_heads, d.n_kv_heads, d.head_dim, d.dtype)
+    return plan, out
+
+
+def _check_case(case, ratios=None):
+    d = case.dims
+    say(f"[layer] case={case.name} dtype={d.dtype} requests={len(case.requests)}")
+    run = SparseXLayerRun(case, ratios=ratios).run()
+    torch.cuda.synchronize()
+    guard_before = None
+    seq = run.plan["seq_start"]
+    k_all = run.plan["k"]
+    sel = run.sel_rows.cpu().numpy()
+    act = run.act_rows.cpu().numpy()
+    o_gpu = run.o.float().cpu().double().numpy()
+    sc_gpu = run.scores.cpu().double().numpy()
+    sel_off, act_off = 0, 0
+    for r in range(len(case.requests)):
+        ratio = (ratios or [rq.ratio for rq in case.requests])[r]
+        plan, ref = _oracle_request(case, r, ratio)
+        T = plan["T"]
+        k = plan["k"]
+        assert k == k_all[r]
+        s_gpu = sc_gpu[seq[r]:seq[r] + T]
+        s_ref = ref["scores"]
+        tol = 1e-4 * s_ref.max()
+        assert np.all(np.abs(s_gpu - s_ref) <= 2e-3 * s_ref + tol), \
+            f"scores: max abs err {np.max(np.abs(s_gpu - s_ref)):.3g}"
+        g_sel = sel[sel_off:sel_off + k] - seq[r]
+        nd = selection_contract(g_sel, s_ref, plan["cand"], k, tol + 2e-3 * s_ref.max())
+        say(f"  request {r}: T={T} |I_nr|={len(plan['sq'])} k={k} selection differences={nd}")
+        A_gpu = act[act_off:act_off + len(plan["sq"]) + k] - seq[r]
+        assert np.array_equal(A_gpu, np.union1d(plan["sq"], g_sel))
+        # output rows common to both active sets
+        common, gi, ri = np.intersect1d(A_gpu, ref["A"], return_indices=True)
+        og = o_gpu[act_off + gi]
+        orf = ref["O_exact"][ri]
+        if d.dtype == "bf16":
+            assert_close_bf16(og, orf, what=f"O request {r}")
+        else:
+            assert_close_f32(og, orf, what=f"O request {r}")
+        # final mixed cache: identical where both sides made the same choice
+        Kg, Vg = run.request_cache(r)
+        same = np.ones(T, dtype=bool)
+        same[np.setxor1d(g_sel, ref["S"])] = False
+        if d.dtype == "bf16":
+            assert_close_bf16(Kg[same], ref["K"][same], what="K cache")
+            assert_close_bf16(Vg[same], ref["V"][same], what="V cache")
+        else:
+            assert_close_f32(Kg[same], ref["K"][same], what="K cache")
+            assert_close_f32(Vg[same], ref["V"][same], what="V cache")
+        sel_off += k
+        act_off += len(plan["sq"]) + k
+    # guard pages were never written
+    gp = torch.as_tensor(run.guard_pages.astype(np.int64), device=run.pool.k.device)
+    kb = run.pool.k.index_select(0, gp)
+    vb = run.pool.v.index_select(0, gp)
+    if d.dtype == "bf16":
+        assert bool((kb.view(torch.int16) == 0x7FA5).all()) and bool((vb.view(torch.int16) == 0x7FA5).all())
+    else:
+        assert bool(torch.isnan(kb).all()) and bool(torch.isnan(vb).all())
+    return run
+
+
+def test_layer_tiny_fp32():
+    """hidden 256, 4/1 heads, d 64, fp32; two 64-token segments + 16 new."""
+    _check_case(synth.tiny_case())
+
+
+@pytest.mark.parametrize("ratio", [(0, 100), (100, 100)])
+def test_layer_tiny_fp32_extreme_ratios(ratio):
+    _check_case(synth.tiny_case(ratio=ratio, cache_noise=0.5))
+
+
+def test_layer_llama_bf16():
+    """Llama-3-8B-shaped layer: 8 x 512 reused + 256 new, 15%."""
+    _check_case(synth.llama_layer_case())
+
+
+def test_layer_llama_bf16_context_dependent_caches():
+    _check_case(synth.llama_layer_case(n_seg=3, cache_noise=0.5, ratio=(30, 100)))
+
+
+def test_layer_agent_batch_fallback_bf16():
+    """Several requests, no new tokens: the tail fallback supplies I_nr."""
+    case = synth.agent_case(n_req=3, target=2500, n_pool=10, lmax=512)
+    _check_case(case)
