@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark: SparseX prefill on the 32K RAG mix, one MI355X.
+
+Workload: a 32-layer Llama-3-8B-shaped attention stack in bf16 (hidden 4096,
+32 q / 8 kv heads, head_dim 128, RoPE theta 5e5) over one request made of a
+reused 512-token system segment, 16 reused 1920-token passages and a
+256-token new query (31,488 tokens).  Layers 0-3 run full attention; the
+Sparse-Q estimation at layer 3 selects 10% of the reused tokens; layers 4-31
+realign, recompute the active rows and run sparse attention.  Inputs are
+seeded synthetic values (no dataset, random weights), resident in HBM before
+timing starts.
+
+A step is one prefill pass of the batch through all 32 layers.  The headline
+value is prefill tokens/s per sparse layer: T / t_layer with
+t_layer = (sum over sparse layers of realign + recompute + sparse attention
++ the one selection) / 28, all from HIP events on the launch stream.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s per layer @32K (sparse recompute); attn % of MFMA bf16 peak"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_rag32k_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "segment_level_kv_amd", "csrc", "attention.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--threshold", type=int, default=4)
+    return ap.parse_args()
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per sparse-attention launch from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("attention_hip_sha256_16") != source_hash(ATTN_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(dims, plan, n_sparse: int, T: int, reused: int, seed: int = 4242):
+    """The float64 oracle on a bounded sample of one sparse layer of the same
+    workload, scaled to tokens/s per layer.  Sample: realign of one
+    1920-token passage, projection of 16 active rows, attention of 8 active
+    rows, and 4 Sparse-Q rows of the selection probe (amortised over the
+    sparse layers); each part is scaled by its share of the layer's work."""
+    import oracle
+    from segment_level_kv_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()
+                     if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    rng = np.random.default_rng(seed)
+    hkv, hq, d = dims.n_kv_heads, dims.n_q_heads, dims.head_dim
+    sq = plan["sq_rows"].astype(np.int64)
+    cand = np.flatnonzero(plan["tok_class"] == 0)
+    k = int(plan["k"][0])
+    S = np.sort(rng.choice(cand, size=k, replace=False))
+    A = np.union1d(sq, S)
+    R = reused
+    K = synth.to_storage(rng.standard_normal((T, hkv, d)), "bf16")
+    V = synth.to_storage(rng.standard_normal((T, hkv, d)), "bf16")
+    t = {}
+    # realign: one passage
+    t0 = time.perf_counter()
+    oracle.realign_segment(K[:1920], V[:1920], 512, 2048, dims.theta, "bf16")
+    t["realign"] = (time.perf_counter() - t0) * (R / 1920)
+    # recompute: 16 rows
+    x = synth.to_storage(synth._rmsnormed_gaussian(rng, 16, dims.hidden, dims.eps), "bf16")
+    wq, wk, wv = synth._weights(rng, dims)
+    t0 = time.perf_counter()
+    oracle.project_rows(x, wq, wk, wv, S[:16], dims.theta, hq, hkv, d, "bf16")
+    t["recompute"] = (time.perf_counter() - t0) * (len(A) / 16)
+    # attention: 8 active rows, scaled by key count
+    rows = np.sort(rng.choice(A, size=8, replace=False))
+    q = synth.to_storage(rng.standard_normal((8, hq, d)), "bf16")
+    t0 = time.perf_counter()
+    oracle.causal_attention(q, rows, K, V)
+    t["attn"] = (time.perf_counter() - t0) * (np.sum(A + 1) / np.sum(rows + 1))
+    # selection probe: 4 Sparse-Q rows (LSE + scores), amortised
+    qs = synth.to_storage(rng.standard_normal((4, hq, d)), "bf16")
+    t0 = time.perf_counter()
+    _, lse = oracle.causal_attention(qs, sq[:4], K, V)
+    oracle.attention_mass_scores(qs, sq[:4], K, lse)
+    t["select"] = (time.perf_counter() - t0) * (len(sq) / 4) / n_sparse
+    layer_s = sum(t.values())
+    return {"value": T / layer_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": ("float64 NumPy oracle, one sparse layer of the same workload: realign of one "
+                       "1920-token passage (x R/1920), projection of 16 active rows (x |A|/16), "
+                       "attention of 8 active rows (x key-count share), 4 Sparse-Q probe rows "
+                       "(x 256/4, amortised over the sparse layers)"),
+            "seconds_per_layer": layer_s, "parts_s": {k_: round(v, 4) for k_, v in t.items()}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from segment_level_kv_amd import synth
+    from segment_level_kv_amd.stack import HybridStackRun, phase_counts, phase_ms
+
+    dims = synth.LLAMA8B
+    seg_lengths, layout, p_src = synth.rag_layout()
+    seg_len = {i: n for i, n in enumerate(seg_lengths)}
+    seg_p = {i: p for i, p in enumerate(p_src)}
+    n_layers, t = args.layers, args.threshold
+    n_tok = sum(seg_lengths) + 256
+    n_cache = sum(seg_lengths)
+    dev = "cuda"
+    inputs = synth.TorchStackInputs(1003, dims, n_layers, n_tok, n_cache, t, dev)
+    run = HybridStackRun(dims, n_layers, t, [layout], seg_len, seg_p, [(10, 100)], inputs, dev)
+    run.build_caches()
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        run.forward()
+    torch.cuda.synchronize()
+
+    timer = {}
+    step_ev = []
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        run.forward(timer)
+        b.record()
+        step_ev.append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    ms_step = float(np.mean([a.elapsed_time(b) for a, b in step_ev]))
+    ph = phase_ms(timer)
+    cnt = phase_counts(timer)
+    K = args.steps
+    n_sparse = n_layers - t
+    T = run.n_tok
+    sparse_ms = (ph.get("realign", 0) + ph.get("recompute", 0) + ph.get("sparse_attn", 0)
+                 + ph.get("select", 0)) / K
+    t_layer_ms = sparse_ms / n_sparse
+    value = T / (t_layer_ms * 1e-3)
+
+    # sparse attention roofline: unmasked MACs of QK^T and PV
+    act = run.act_rows[:run.n_act].cpu().numpy().astype(np.int64)
+    pos = act - run.seq_start_h[0]
+    flops = 4.0 * dims.head_dim * dims.n_q_heads * float(np.sum(pos + 1))
+    attn_ms = ph["sparse_attn"] / cnt["sparse_attn"]
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+    # other phases (per launch)
+    reused = sum(seg_lengths)
+    realign_bytes = 2.0 * reused * dims.n_kv_heads * dims.head_dim * 2 * 2   # K+V read + write
+    realign_ms = ph["realign"] / cnt["realign"]
+    rec_flops = 2.0 * run.n_act * dims.qkv_rows * dims.hidden
+    rec_ms = ph["recompute"] / cnt["recompute"]
+    full_rec_ms = ph.get("full_recompute", 0) / max(cnt.get("full_recompute", 1), 1)
+    full_attn_ms = ph.get("full_attn", 0) / max(cnt.get("full_attn", 1), 1)
+    full_attn_flops = 4.0 * dims.head_dim * dims.n_q_heads * (T * (T + 1) / 2)
+    sel_ms = ph.get("select", 0) / max(cnt.get("select", 1), 1)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("rag32k: 32-layer Llama-3-8B-shaped attention stack (hidden 4096, 32/8 heads, "
+                         "head_dim 128), 512 reused system + 16x1920 reused passages + 256 new "
+                         f"= {T} tokens, full layers 0-{t - 1}, sparse {t}-{n_layers - 1}, ratio 10%"),
+            "tokens": T, "active_rows": int(run.n_act), "selected": int(run.n_sel),
+            "sparse_q_rows": int(run.n_sq), "layers": n_layers, "threshold": t, "page_size": 16,
+        },
+        "attn_pct_mfma_bf16_peak": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "kernel": "sx_sparse_attn (attn_bf16<4,true>)",
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "flops_per_launch": flops, "avg_launch_ms": round(attn_ms, 4),
+        },
+        "phases_ms_per_launch": {
+            "realign": round(realign_ms, 4), "recompute_active": round(rec_ms, 4),
+            "sparse_attn": round(attn_ms, 4), "select": round(sel_ms, 4),
+            "full_recompute": round(full_rec_ms, 4), "full_attn": round(full_attn_ms, 4),
+        },
+        "phases_rate": {
+            "realign_GBps": round(realign_bytes / (realign_ms * 1e-3) / 1e9, 1),
+            "recompute_active_TFLOPs": round(rec_flops / (rec_ms * 1e-3) / 1e12, 1),
+            "full_attn_TFLOPs": round(full_attn_flops / (full_attn_ms * 1e-3) / 1e12, 1) if full_attn_ms else None,
+            "full_recompute_TFLOPs": round(2.0 * T * dims.qkv_rows * dims.hidden / (full_rec_ms * 1e-3) / 1e12, 1) if full_rec_ms else None,
+        },
+        "full_stack_tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "sparse_layer_ms": round(t_layer_ms, 4),
+        "full_layer_ms": round(full_rec_ms + full_attn_ms, 4),
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(dims, run.plan, n_sparse, T, reused)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -293,3 +293,43 @@ def page_permutation(seed: int, n_pages: int) -> np.ndarray:
 def gaussian(seed: int, shape, scale: float = 1.0) -> np.ndarray:
     """Plain seeded N(0, scale^2) float64 array (for kernel-level inputs)."""
     return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------------------
+# device-side generation for large workloads (same recipe, torch generator)
+# ---------------------------------------------------------------------------
+
+def torch_rmsnormed_rows(gen, n: int, hidden: int, eps: float, dtype, device):
+    """N(0,1) rows, RMSNorm with unit gain, cast to the storage type."""
+    import torch
+    x = torch.randn((n, hidden), generator=gen, device=device, dtype=torch.float32)
+    x = x * torch.rsqrt(torch.mean(x * x, dim=1, keepdim=True) + eps)
+    return x.to(dtype)
+
+
+def torch_weights(gen, dims: Dims, dtype, device):
+    """W_qkv rows (W_q, W_k, W_v) ~ N(0, 1/hidden) in the storage type."""
+    import torch
+    w = torch.randn((dims.qkv_rows, dims.hidden), generator=gen, device=device, dtype=torch.float32)
+    return (w * (1.0 / np.sqrt(dims.hidden))).to(dtype)
+
+
+class TorchStackInputs:
+    """Per-layer (x, w_qkv, x_cache) generated once on the device."""
+
+    def __init__(self, seed: int, dims: Dims, n_layers: int, n_tok: int, n_cache_tok: int,
+                 threshold: int, device):
+        import torch
+        dt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
+        gen = torch.Generator(device=device)
+        gen.manual_seed(seed)
+        self.layers = []
+        for l in range(n_layers):
+            x = torch_rmsnormed_rows(gen, n_tok, dims.hidden, dims.eps, dt, device)
+            w = torch_weights(gen, dims, dt, device)
+            xc = (torch_rmsnormed_rows(gen, n_cache_tok, dims.hidden, dims.eps, dt, device)
+                  if l >= threshold else None)
+            self.layers.append((x, w, xc))
+
+    def __call__(self, l: int):
+        return self.layers[l]

@@ -3,8 +3,11 @@
 Every entry point is called through the C ABI (libsx.so) and compared with
 the oracle function that defines the same step.  Tolerances:
   fp32 storage: max |g - r| <= 1e-4 * max |r| per tensor;
-  bf16 storage: |g - r| <= 1e-2 + 2^-8 |r| per element (one bf16 rounding of
-  a value >= 4 alone exceeds 1e-2);
+  bf16 outputs against the unrounded oracle: |g - r| <= 1e-2 + 2^-8 |r|
+  (the store itself adds up to half a bf16 step, 2^-8 |r|, which alone
+  exceeds 1e-2 for |r| >= 2.56);
+  bf16 stored values against the oracle's rounded values: one bf16 step per
+  storage rounding, |g - r| <= 1e-2 + 2^-7 |r|;
   integer/index results and page-table writes: bit-exact.
 """
 
@@ -16,7 +19,7 @@ import oracle
 from segment_level_kv_amd import _lib as L
 from segment_level_kv_amd import layer as LY
 from segment_level_kv_amd import synth
-from tests.gpu_util import (assert_close_bf16, assert_close_f32, bf16_ulps, say,
+from tests.gpu_util import (BF16_STEP_REL, assert_close_bf16, assert_close_f32, bf16_ulps, say,
                             selection_contract)
 
 pytestmark = pytest.mark.gpu
@@ -101,7 +104,7 @@ def test_realign_parity_and_copy_semantics(shape):
             assert np.array_equal(kg, kr), "delta 0 must copy K bit-exactly"
         if dims.dtype == "bf16":
             assert bf16_ulps(kg, kr).max() <= 1
-            assert_close_bf16(kg, kr, what="realigned K")
+            assert_close_bf16(kg, kr, rel=BF16_STEP_REL, what="realigned K")
         else:
             assert_close_f32(kg, kr, what="realigned K")
         for j in range(s["len"]):
@@ -129,7 +132,7 @@ def test_recompute_parity_and_scatter(shape, n_rows):
     w = np.concatenate(case_w, axis=0)
     rows = np.sort(rng.choice(n_tok, size=n_rows, replace=False)).astype(np.int32)
     rng.shuffle(rows)                             # row order need not be sorted
-    n_pages = 80
+    n_pages = 100
     pool = LY.PagePool.alloc(n_pages, dims, DEV)
     perm = rng.permutation(n_pages).astype(np.int32)
     bt = perm[:2 * 44].reshape(2, 44)
@@ -155,8 +158,11 @@ def test_recompute_parity_and_scatter(shape, n_rows):
     vg = np.stack([av[bt[r, i // 16], :, :, i % 16] for r, i in zip(req, idx)])
     if dims.dtype == "bf16":
         for g_, r_, nm in [(qg, qr, "Q"), (kg, kr, "K"), (vg, vr, "V")]:
-            assert bf16_ulps(g_, r_).max() <= 1, nm
-            assert_close_bf16(g_, r_, what=nm)
+            # away from zero the two roundings differ by at most one step; near
+            # zero cancellation in the dot product makes steps meaningless
+            big = np.abs(r_) >= 1e-2
+            assert bf16_ulps(g_[big], r_[big]).max() <= 1, nm
+            assert_close_bf16(g_, r_, rel=BF16_STEP_REL, what=nm)
     else:
         assert_close_f32(qg, qr, what="Q")
         assert_close_f32(kg, kr, what="K")
