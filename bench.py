@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--threshold", type=int, default=4)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain elementwise copy (torch.neg) of this many MiB of fp32 "
+                         "before the timed region, as the byte-counter reference for rocprofv3")
     return ap.parse_args()
 
 
@@ -149,6 +152,13 @@ def main():
     run = HybridStackRun(dims, n_layers, t, [layout], seg_len, seg_p, [(10, 100)], inputs, dev)
     run.build_caches()
     torch.cuda.synchronize()
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         run.forward()

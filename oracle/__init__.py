@@ -19,7 +19,7 @@ Parity status per function (see each docstring):
   round_bf16, rope_rotate, realign_segment, plan_request, project_rows,
   causal_attention, attention_mass_scores, select_topk, sparse_layer,
   full_layer -- pinned by tests/test_oracle_pins.py and
-  tests/test_bruteforce.py against closed forms, invariants, library
+  tests/test_oracle_layer.py against closed forms, invariants, library
   routines and brute force.
 """
 
