@@ -30,12 +30,15 @@ CFLAGS = [
     "-Wall", "-Wno-unused-result",
 ]
 SOURCES = ["api.cpp", "rope_realign.hip", "recompute_kv.hip", "attention.hip", "select.hip"]
+# Per-source extra flags.  The attention softmax never produces NaN (masked
+# logits are -inf), so max reductions need no NaN quieting.
+EXTRA = {"attention.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *CFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

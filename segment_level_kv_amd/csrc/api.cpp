@@ -236,8 +236,8 @@ size_t sx_workspace_bytes(int32_t op, const sx_dims* dims, int32_t n_tok, int32_
   switch (op) {
     case SX_OP_SELECT: return select_ws_bytes(*dims, n_tok, n_rows, n_req);
     case SX_OP_TOPK: return topk_ws_bytes(n_tok, n_req);
-    case SX_OP_SPARSE_ATTN: return dims->dtype == SX_BF16 ? attn_ws_bytes(n_rows, n_req) : 0;
-    case SX_OP_FULL_ATTN: return dims->dtype == SX_BF16 ? attn_ws_bytes(n_tok, n_req) : 0;
+    case SX_OP_SPARSE_ATTN: return attn_ws_bytes(*dims, n_rows, n_req, true);
+    case SX_OP_FULL_ATTN: return attn_ws_bytes(*dims, n_tok, n_req, true);
     default: return 0;
   }
 }

@@ -4,24 +4,35 @@
 // selected rows after it; §4.5 last paragraph: reused blocks are read through
 // the block table, recomputed tokens take the normal attention path).
 //
-// bf16 kernel (gfx950): one workgroup = one query tile (64 consecutive
-// active rows of one request) x one kv head; wave w owns query head
-// g*G + w for all 64 rows, so the G heads sharing a kv head share every K/V
-// block staged in LDS.  Per 64-key block:
-//   S^T[key][q] = K . Q^T        (v_mfma_f32_32x32x16_bf16, Q in registers)
-//   online softmax over the key axis, which sits in registers (16 keys per
-//   lane per 32-key block; one cross-half exchange for the row max)
-//   O^T[d][q] += V^T . P^T        (P^T straight from the S^T accumulators)
-// Keys are permuted inside each 32-key block when K rows are loaded, so that
-// the accumulator registers of S^T are exactly the B operand of the PV
-// product (8 consecutive keys per lane half).  V pages are stored [d][slot],
-// so the V^T operand is one contiguous 16-byte LDS read.  K/V blocks are
-// double-buffered in LDS with register prefetch; only blocks that reach
-// past the tile's first row apply the causal mask.
+// bf16 path (gfx950)
+// ------------------
+// Work unit: one kv head g and one query tile of (row, head) pairs: M
+// consecutive active rows of one request times the G query heads of g
+// (M = 256 / G, so a tile is at most 256 pairs, 64 per wave).  Long tiles
+// are split along the key axis into chunks so that every compute unit gets
+// several units of similar length; each chunk is one workgroup.  A small
+// single-workgroup kernel builds the list of (tile, key chunk) items on the
+// device (the active rows are device data) and orders it longest first; a
+// merge kernel combines the chunks of split tiles in chunk order, so results
+// do not depend on scheduling.
 //
-// Scheduling: tiles are ordered longest first (last tile of each request
-// first), and workgroup b takes kv head b % Hkv so that with 8 kv heads each
-// XCD streams a single head's K/V through its L2.
+// Per 64-key block and wave (64 pairs):
+//   S^T[key][pair] = K . Q^T    32 x v_mfma_f32_32x32x16_bf16, Q in registers
+//   online softmax over the key axis, which lies inside a lane (32 keys per
+//   lane and pair, the other 32 in the partner lane half)
+//   O^T[d][pair] += V^T . P^T   32 x v_mfma_f32_32x32x16_bf16
+// Keys are permuted inside each 32-key block when K is read from LDS so that
+// the S^T accumulators are directly the B operand of the PV product.  The
+// QK^T product of block j+1 is issued before the softmax of block j so that
+// its MFMAs overlap the exponentials.  The running maximum is raised only
+// when a block's maximum exceeds it by more than 2^8 (in the exp2 domain),
+// so O is rarely rescaled; exp2 arguments then stay below 8.
+// K/V blocks stream through a 3-stage LDS ring (one barrier per block);
+// the page ids of a block are wave-uniform and come through the scalar
+// cache.  Workgroup b takes kv head b % Hkv: with 8 kv heads each XCD streams
+// one head's K/V through its own L2.
+#include <type_traits>
+
 #include "sx_device.hpp"
 #include "sx_internal.hpp"
 
@@ -30,276 +41,660 @@ namespace sx {
 namespace {
 
 constexpr int KB = 64;                 // keys per block
-constexpr int LDK = 128 + 8;           // padded K row (bf16 elements)
-constexpr int LDV = KB + 8;            // padded V^T row
+constexpr int NSTAGE = 3;              // LDS ring depth
+constexpr int PAIRS = 256;             // (row, head) pairs per workgroup
+constexpr int kTargetItems = 768;      // work items aimed for (about 3 per CU)
+constexpr int kMinChunk = 1024;        // shortest key chunk of a split tile
+constexpr int kBuildThreads = 1024;
+constexpr int kSortBuckets = 2048;     // item length buckets (64 keys each)
 
-template <int G>
-struct AttnSmem {
-  uint16_t k[2][KB][LDK];
-  uint16_t v[2][128][LDV];
+struct Stage {
+  uint16_t k[KB][128];        // 64 key rows, 16-byte chunks XOR-swizzled by row
+  uint16_t v[4][128][16];     // 4 V page-heads [d][slot], halves swizzled by d
 };
 
-// Tile table: tiles of kTileRows rows per request; ordered by rank from the
-// request's end (largest positions first), then by request.
-// Rows outside [0, n_rows) (an inconsistent row_start) produce no tile, and
-// at most max_tiles tiles are written.
-__global__ __launch_bounds__(256) void build_tiles(const int32_t* __restrict__ row_start, int n_req,
-                                                   int n_rows, int max_tiles,
-                                                   AttnTile* __restrict__ tiles, int* __restrict__ n_tiles) {
-  extern __shared__ int cnt[];
-  for (int r = threadIdx.x; r < n_req; r += blockDim.x) {
-    const int a = max(row_start[r], 0), b = min(row_start[r + 1], n_rows);
-    const int n = b - a;
-    cnt[r] = n > 0 ? (n + kTileRows - 1) / kTileRows : 0;
+// One workgroup's work: query rows [row0, row0 + nrows) (indices into the
+// row list) of request req, keys [k0, k1).  slot < 0: the tile is not split
+// and the workgroup writes the final output; otherwise partial results go to
+// partial slot `slot`.
+struct AttnItem {
+  int32_t req, row0, nrows, k0, k1, slot, pad0, pad1;
+};
+struct MergeTile {
+  int32_t row0, nrows, slot0, n_chunks;
+};
+struct TileInfo {
+  int32_t req, row0, nrows, pmin, pmax, n_chunks, item0, slot0;
+};
+
+int rows_per_tile(int G) { return PAIRS / G; }
+int items_per_head(int hkv) { return (kTargetItems + hkv - 1) / hkv; }
+
+struct WsLayout {
+  size_t counters, tiles, items, merges, part_ml, part_o, total;
+  int max_tiles, max_items;
+};
+
+WsLayout ws_layout(int n_rows, int n_req, int G, int hkv, bool with_o) {
+  WsLayout w;
+  const int M = rows_per_tile(G);
+  w.max_tiles = (n_rows + M - 1) / M + n_req;
+  w.max_items = 2 * w.max_tiles + items_per_head(hkv);
+  size_t off = 0;
+  w.counters = off; off += align256(4 * sizeof(int32_t));
+  w.tiles = off;    off += align256((size_t)w.max_tiles * sizeof(TileInfo));
+  w.items = off;    off += align256((size_t)w.max_items * sizeof(AttnItem));
+  w.merges = off;   off += align256((size_t)w.max_tiles * sizeof(MergeTile));
+  w.part_ml = off;  off += align256((size_t)w.max_items * hkv * PAIRS * 2 * sizeof(float));
+  w.part_o = off;
+  if (with_o) off += align256((size_t)w.max_items * hkv * PAIRS * 128 * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+// Block-wide exclusive scan over kBuildThreads threads; *total gets the sum.
+__device__ int build_scan(int v, int* sh, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[w] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int i = 0; i < kBuildThreads / 64; ++i) {
+    const int s = sh[i];
+    before += (i < w) ? s : 0;
+    tot += s;
   }
   __syncthreads();
-  int total = 0;
-  for (int r = 0; r < n_req; ++r) total += cnt[r];
-  if (threadIdx.x == 0) *n_tiles = min(total, max_tiles);
-  for (int r = 0; r < n_req; ++r) {
-    const int c = cnt[r];
-    for (int t = threadIdx.x; t < c; t += blockDim.x) {
-      int pos = 0;
-      for (int r2 = 0; r2 < n_req; ++r2) pos += min(cnt[r2], t) + ((r2 < r && cnt[r2] > t) ? 1 : 0);
-      if (pos >= max_tiles) continue;
+  *total = tot;
+  return before + x - v;
+}
+
+// Builds the (tile, key chunk) work list.  One workgroup.
+//   rows == NULL: row m is packed token m.  Positions are row - seq_start[r].
+// Counters: [0] items, [1] merge tiles.  Dynamic LDS: (n_req + 1) ints.
+__global__ __launch_bounds__(kBuildThreads) void build_work(
+    const int32_t* __restrict__ row_start, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ seq_start, int n_req, int n_rows, int M, int items_target,
+    int max_tiles, int max_items, int allow_split, TileInfo* __restrict__ tiles,
+    AttnItem* __restrict__ items, MergeTile* __restrict__ merges, int32_t* __restrict__ counters) {
+  extern __shared__ int roff[];              // first tile of each request
+  __shared__ int sh_scan[kBuildThreads / 64];
+  __shared__ int hist[kSortBuckets];
+  __shared__ long long s_work[kBuildThreads / 64];
+  const int tid = threadIdx.x;
+
+  // ---- tiles per request -> offsets ---------------------------------------------
+  int n_tiles = 0;
+  for (int r0 = 0; r0 < n_req; r0 += kBuildThreads) {
+    const int r = r0 + tid;
+    int c = 0;
+    if (r < n_req) {
       const int a = max(row_start[r], 0), b = min(row_start[r + 1], n_rows);
-      const int row0 = a + (c - 1 - t) * kTileRows;
-      AttnTile tl;
-      tl.req = r;
-      tl.row0 = row0;
-      tl.nrows = min(kTileRows, b - row0);
-      tl.pad = 0;
-      tiles[pos] = tl;
+      c = b > a ? (b - a + M - 1) / M : 0;
     }
+    int tot;
+    const int off = n_tiles + build_scan(c, sh_scan, &tot);
+    if (r < n_req) roff[r] = off;
+    n_tiles += tot;
+  }
+  if (tid == 0) roff[n_req] = n_tiles;
+  __syncthreads();
+  n_tiles = min(n_tiles, max_tiles);
+
+  // ---- one thread per tile --------------------------------------------------------
+  long long work = 0;
+  for (int t = tid; t < n_tiles; t += kBuildThreads) {
+    int lo = 0, hi = n_req - 1;              // request r with roff[r] <= t < roff[r+1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (roff[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int r = lo;
+    const int a = max(row_start[r], 0), b = min(row_start[r + 1], n_rows);
+    const int s0 = seq_start[r];
+    const int row0 = a + (t - roff[r]) * M;
+    const int nr = min(M, b - row0);
+    const int pmin = (rows ? rows[row0] : row0) - s0;
+    const int pmax = (rows ? rows[row0 + nr - 1] : row0 + nr - 1) - s0;
+    TileInfo ti_;
+    ti_.req = r;
+    ti_.row0 = row0;
+    ti_.nrows = nr;
+    ti_.pmin = max(pmin, 0);
+    ti_.pmax = max(pmax, ti_.pmin);
+    ti_.n_chunks = 1;
+    ti_.item0 = 0;
+    ti_.slot0 = -1;
+    tiles[t] = ti_;
+    work += (long long)ti_.pmax + 1;
+  }
+  // total key work -> chunk length
+  {
+    long long x = work;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    if ((tid & 63) == 0) s_work[tid >> 6] = x;
+  }
+  __syncthreads();   // tiles[] written by this workgroup are visible after the barrier
+  long long total_work = 0;
+  for (int i = 0; i < kBuildThreads / 64; ++i) total_work += s_work[i];
+  const bool split = allow_split && n_tiles < items_target;
+  long long ck = split ? (total_work + items_target - 1) / items_target : 0x3fffffff;
+  ck = ((ck + KB - 1) / KB) * KB;
+  if (ck < kMinChunk) ck = kMinChunk;
+  const int chunk = (int)min(ck, 0x3fffffffLL);
+
+  // ---- chunks per tile, item and slot offsets -------------------------------------
+  int item_base = 0, slot_base = 0, merge_base = 0;
+  for (int t0 = 0; t0 < n_tiles; t0 += kBuildThreads) {
+    const int t = t0 + tid;
+    int nc = 0;
+    if (t < n_tiles) {
+      const int last_start = (tiles[t].pmin / KB) * KB;
+      nc = split && last_start > 0 ? 1 + (last_start + chunk - 1) / chunk : 1;
+    }
+    int tot_i, tot_s, tot_m;
+    const int io = item_base + build_scan(nc, sh_scan, &tot_i);
+    const int so = slot_base + build_scan(nc > 1 ? nc : 0, sh_scan, &tot_s);
+    const int mo = merge_base + build_scan(nc > 1 ? 1 : 0, sh_scan, &tot_m);
+    if (t < n_tiles) {
+      tiles[t].n_chunks = nc;
+      tiles[t].item0 = io;
+      tiles[t].slot0 = nc > 1 ? so : -1;
+      if (nc > 1) {
+        MergeTile mt;
+        mt.row0 = tiles[t].row0;
+        mt.nrows = tiles[t].nrows;
+        mt.slot0 = so;
+        mt.n_chunks = nc;
+        merges[mo] = mt;
+      }
+    }
+    item_base += tot_i;
+    slot_base += tot_s;
+    merge_base += tot_m;
+  }
+  const int n_items = min(item_base, max_items);
+
+  // ---- items, counting-sorted by length (longest first) ----------------------------
+  for (int i = tid; i < kSortBuckets; i += kBuildThreads) hist[i] = 0;
+  __syncthreads();
+  // chunk c of tile t: the last chunk starts at the block holding pmin so that
+  // every row sees at least one key of every chunk; earlier chunks step back
+  // by `chunk` keys (the first one may be shorter).
+  auto chunk_range = [&](const TileInfo& T, int c, int& k0, int& k1) {
+    if (T.n_chunks == 1) {
+      k0 = 0;
+      k1 = T.pmax + 1;
+      return;
+    }
+    const int last_start = (T.pmin / KB) * KB;
+    const int back = T.n_chunks - 1 - c;       // chunks after this one
+    if (back == 0) {
+      k0 = last_start;
+      k1 = T.pmax + 1;
+    } else {
+      k1 = last_start - (back - 1) * chunk;
+      k0 = max(0, k1 - chunk);
+    }
+  };
+  for (int t = tid; t < n_tiles; t += kBuildThreads) {
+    const TileInfo T = tiles[t];
+    for (int c = 0; c < T.n_chunks; ++c) {
+      int k0, k1;
+      chunk_range(T, c, k0, k1);
+      const int bkt = min((k1 - k0 - 1) / KB, kSortBuckets - 1);
+      atomicAdd(&hist[kSortBuckets - 1 - bkt], 1);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the histogram (longest bucket first)
+  {
+    constexpr int PER = kSortBuckets / kBuildThreads;
+    int loc[PER], s = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      loc[i] = hist[tid * PER + i];
+      s += loc[i];
+    }
+    int tot;
+    int pre = build_scan(s, sh_scan, &tot);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      hist[tid * PER + i] = pre;
+      pre += loc[i];
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < n_tiles; t += kBuildThreads) {
+    const TileInfo T = tiles[t];
+    for (int c = 0; c < T.n_chunks; ++c) {
+      int k0, k1;
+      chunk_range(T, c, k0, k1);
+      const int bkt = min((k1 - k0 - 1) / KB, kSortBuckets - 1);
+      const int pos = atomicAdd(&hist[kSortBuckets - 1 - bkt], 1);
+      if (pos >= max_items) continue;
+      AttnItem it;
+      it.req = T.req;
+      it.row0 = T.row0;
+      it.nrows = T.nrows;
+      it.k0 = k0;
+      it.k1 = k1;
+      it.slot = T.n_chunks > 1 ? T.slot0 + c : -1;
+      it.pad0 = T.pmin;
+      it.pad1 = T.pmax;
+      items[pos] = it;
+    }
+  }
+  if (tid == 0) {
+    counters[0] = n_items;
+    counters[1] = merge_base;
   }
 }
 
-template <int G, bool WITH_O>
-__global__ __launch_bounds__(G * 64) void attn_bf16(
+__device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32); }
+
+template <bool WITH_O>
+__global__ __launch_bounds__(256, 1) void attn_fwd(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_index,
     const int32_t* __restrict__ rows, sx_layout lay, int n_pages,
-    const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool, int hkv,
-    uint16_t* __restrict__ o, float* __restrict__ lse, const AttnTile* __restrict__ tiles,
-    const int* __restrict__ n_tiles, float scale_log2) {
-  constexpr int NT = G * 64;
-  constexpr int KU = (KB * 16 + NT - 1) / NT;      // 16-byte K units per thread per block
-  constexpr int VU = (128 * 8 + NT - 1) / NT;      // 16-byte V units per thread per block
+    const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool, int hkv, int G,
+    uint16_t* __restrict__ o, float* __restrict__ lse, const AttnItem* __restrict__ items,
+    const int32_t* __restrict__ counters, float* __restrict__ part_ml,
+    float* __restrict__ part_o, int max_slots, float scale_log2) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  AttnSmem<G>& sm = *reinterpret_cast<AttnSmem<G>*>(smem_raw);
+  Stage* st = reinterpret_cast<Stage*>(smem_raw);
 
   const int g = blockIdx.x % hkv;
-  const int ti = blockIdx.x / hkv;
-  if (ti >= *n_tiles) return;
-  const AttnTile tl = tiles[ti];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ii = blockIdx.x / hkv;
+  if (ii >= counters[0] || n_pages <= 0) return;
+  const AttnItem it = items[ii];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hl = lane >> 5;
   const int hq = G * hkv;
-  const int h = g * G + w;
-  const int req = tl.req;
+  const int req = it.req;
   const int seq0 = lay.seq_start[req];
   const int seq_len = lay.seq_start[req + 1] - seq0;
-  auto row_index = [&](int m) { return (rows ? rows[m] : m) - seq0; };
-  const int p_min = row_index(tl.row0);
-  const int p_max = row_index(tl.row0 + tl.nrows - 1);
-  if (p_min < 0 || p_max >= seq_len || p_min > p_max) return;
+  const int k0 = it.k0;
+  const int k1 = min(it.k1, seq_len);
+  if (k1 <= k0) return;
 
-  // ---- this lane's two queries (N-blocks of 32) ---------------------------
-  const int hl = lane >> 5;           // lane half
+  // ---- this lane's two pairs: query operand and positions -------------------
+  const int npairs = it.nrows * G;
   int pos_q[2];
   bf16x8 qf[2][8];
+  int wave_pmin = 0x7fffffff;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int qi = (lane & 31) + 32 * nb;
-    const bool valid = qi < tl.nrows;
-    const int m = tl.row0 + qi;
-    pos_q[nb] = valid ? row_index(m) : p_max;
-    const uint16_t* qp = q + ((size_t)(valid ? (q_index ? q_index[m] : m) : 0) * hq + h) * 128 + hl * 8;
+    const int p = 64 * w + 32 * nb + (lane & 31);
+    const bool valid = p < npairs;
+    const int r = p / G, hh = p - r * G;
+    const int m = it.row0 + (valid ? r : 0);
+    const int row_tok = rows ? rows[m] : m;
+    pos_q[nb] = valid ? row_tok - seq0 : k1 - 1;
+    wave_pmin = min(wave_pmin, pos_q[nb]);
+    const uint16_t* qp = q + ((size_t)(q_index ? q_index[m] : m) * hq + g * G + hh) * 128 + hl * 8;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       u32x4 raw = valid ? *reinterpret_cast<const u32x4*>(qp + kk * 16) : u32x4{0, 0, 0, 0};
       qf[nb][kk] = __builtin_bit_cast(bf16x8, raw);
+      // Q stays in AGPRs for the whole kernel (MFMA reads its B operand from
+      // there), leaving the VGPRs to the softmax and the LDS operands.
+      asm volatile("" : "+a"(qf[nb][kk]));
     }
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) wave_pmin = min(wave_pmin, __shfl_xor(wave_pmin, off));
 
-  // ---- K/V block loader ----------------------------------------------------
+  // ---- K/V stages: global -> LDS directly (global_load_lds_dwordx4) ---------
+  // A wave instruction writes 64 x 16 B = 1 KB of LDS, lane L at byte 16 L.
+  // Wave w copies page w of each 64-key block (its K and V page-heads, 4 KB
+  // each), so page ids are wave-uniform and per-lane offsets are constants.
+  // K stage: 64 key rows x 256 B; row R keeps 16-byte chunk c at slot
+  //   c ^ (R & 15) (16 rows read together hit 16 distinct bank groups).
+  // V stage: the page layout itself, [4 pages][128 d][16 keys]; row d keeps
+  //   its two 16-byte halves (keys 0-7, 8-15) swapped when (d >> 3) is odd.
+  // Pages past the item's last key are replaced by its last page (finite
+  // data, masked or zeroed); an invalid page id reads page 0.
   const int32_t* bt = lay.block_table + (size_t)req * lay.max_pages;
-  const int last_page = p_max / kPage;
-  u32x4 rk[KU], rv[VU];
-  auto gload = [&](int kb) {
+  const int kmax = k1 - 1;                 // last key of this item
+  const int last_pi = min(kmax / kPage, lay.max_pages - 1);
+  typedef __attribute__((address_space(1))) const void* gptr_t;
+  typedef __attribute__((address_space(3))) void* lptr_t;
+  uint32_t koff[4], voff[4];               // byte offsets inside a page-head
 #pragma unroll
-    for (int i = 0; i < KU; ++i) {
-      const int u = tid + NT * i;
-      rk[i] = u32x4{0, 0, 0, 0};
-      if (u < KB * 16) {
-        const int kl = u >> 4, c = u & 15;
-        const int key = kb + kl;
-        const int pi = key / kPage;
-        if (key <= p_max && pi < lay.max_pages) {
-          const int page = bt[pi];
-          if (page >= 0 && page < n_pages)
-            rk[i] = *reinterpret_cast<const u32x4*>(
-                kpool + (((size_t)page * hkv + g) * kPage + (key & (kPage - 1))) * 128 + c * 8);
-        }
-      }
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int slot = 4 * i + (lane >> 4);
+    koff[i] = (uint32_t)(slot * 128 + (((lane & 15) ^ slot) * 8)) * 2u;
+    const int d = 32 * i + (lane >> 1);
+    voff[i] = (uint32_t)(d * 16 + (((lane & 1) ^ ((d >> 3) & 1)) * 8)) * 2u;
+  }
+  const size_t head_bytes = (size_t)kPage * 128 * 2;      // one page-head, 4 KB
+  auto issue_stage = [&](int kb, int s) __attribute__((always_inline)) {
+    int pi = min(kb / kPage + w, last_pi);
+    int pg = bt[pi];
+    pg = (pg >= 0 && pg < n_pages) ? pg : 0;
+    const size_t base = ((size_t)pg * hkv + g) * head_bytes;
+    const unsigned char* kp = reinterpret_cast<const unsigned char*>(kpool) + base;
+    unsigned char* kst = reinterpret_cast<unsigned char*>(&st[s].k[16 * w][0]);
 #pragma unroll
-    for (int i = 0; i < VU; ++i) {
-      const int u = tid + NT * i;
-      rv[i] = u32x4{0, 0, 0, 0};
-      if (u < 128 * 8) {
-        const int d = u >> 3, c8 = u & 7;
-        const int key0 = kb + c8 * 8;               // 8 keys of one page
-        const int pi = key0 / kPage;
-        if (pi <= last_page && pi < lay.max_pages) {
-          const int page = bt[pi];
-          if (page >= 0 && page < n_pages) {
-            u32x4 raw = *reinterpret_cast<const u32x4*>(
-                vpool + (((size_t)page * hkv + g) * 128 + d) * kPage + (key0 & (kPage - 1)));
-            if (key0 + 7 > p_max) {                 // zero keys past the tile's last row
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(kp + koff[i]), (lptr_t)(kst + i * 1024), 16, 0, 0);
+    if (WITH_O) {
+      const unsigned char* vp = reinterpret_cast<const unsigned char*>(vpool) + base;
+      unsigned char* vst = reinterpret_cast<unsigned char*>(&st[s].v[w][0][0]);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                if (key0 + 2 * e > p_max) raw[e] &= 0u;
-                else if (key0 + 2 * e + 1 > p_max) raw[e] &= 0xffffu;
-              }
-            }
-            rv[i] = raw;
-          }
-        }
-      }
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds((gptr_t)(vp + voff[i]), (lptr_t)(vst + i * 1024), 16, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KU; ++i) {
-      const int u = tid + NT * i;
-      if (u < KB * 16) *reinterpret_cast<u32x4*>(&sm.k[buf][u >> 4][(u & 15) * 8]) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VU; ++i) {
-      const int u = tid + NT * i;
-      if (u < 128 * 8) *reinterpret_cast<u32x4*>(&sm.v[buf][u >> 3][(u & 7) * 8]) = rv[i];
+  // Zero the values of keys past kmax in a resident stage (P is 0 there, but
+  // those slots may hold anything, and 0 * NaN would poison O).
+  auto zero_tail = [&](int kb, int s) __attribute__((always_inline)) {
+    const int first = kmax + 1 - kb;       // first key offset to clear
+    if (!WITH_O || first >= KB) return;
+    uint16_t* vs = &st[s].v[0][0][0];
+    for (int u = tid; u < 128 * KB; u += 256) {
+      const int key = u & (KB - 1), d = u >> 6;
+      if (key < first) continue;
+      const int j = key >> 4, kk = key & 15;
+      const int half = (kk >> 3) ^ ((d >> 3) & 1);
+      vs[(j * 128 + d) * kPage + half * 8 + (kk & 7)] = 0;
     }
   };
 
-  // K row loaded by this lane for the S^T A-operand (key permutation inside
-  // a 32-key block: accumulator register v of lane half hl then holds key
-  // 16*(v>>3) + 8*hl + (v&7)).
+  // K row read by this lane for the S^T A operand: inside a 32-key sub-block
+  // the MFMA row mrow holds key kperm(mrow), so that accumulator register v
+  // of lane half hl holds key 16*(v>>3) + 8*hl + (v&7) of the sub-block.
   const int mrow = lane & 31;
   const int kperm = 16 * (mrow >> 4) + 8 * ((mrow >> 2) & 1) + 4 * ((mrow >> 3) & 1) + (mrow & 3);
+
+  // K operand of sub-block h (keys 32h .. 32h+31) of stage s: 8 x 16 B.
+  auto load_k = [&](int s, int h, bf16x8 (&kf)[8]) __attribute__((always_inline)) {
+    const int R = h * 32 + kperm;
+    const uint16_t* kr = &st[s].k[R][0];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int slot = (2 * kk + hl) ^ (R & 15);
+      kf[kk] = *reinterpret_cast<const bf16x8*>(kr + slot * 8);
+    }
+  };
+  // S^T of one query half nb (32 pairs) for a sub-block: 8 MFMAs.
+  auto qk_half = [&](const bf16x8 (&kf)[8], int nb, f32x16& S) __attribute__((always_inline)) {
+    S = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[nb][kk], S, 0, 0, 0);
+  };
 
   f32x16 oacc[4][2];
 #pragma unroll
   for (int md = 0; md < 4; ++md)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) oacc[md][nb] = f32x16{};
-  float m_run[2] = {-INFINITY, -INFINITY};
+  float m_run[2] = {-INFINITY, -INFINITY};   // running max, raw logit units
   float l_run[2] = {0.f, 0.f};
+  float alpha[2] = {1.f, 1.f};
+  const float c = scale_log2;
 
-  const int n_blk = p_max / KB + 1;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int b = 0; b < n_blk; ++b) {
-    const int buf = b & 1;
-    const int kb = b * KB;
-    if (b + 1 < n_blk) gload(kb + KB);
-
-    // S^T = K . Q^T for two 32-key M-blocks
-    f32x16 s[2][2];
+  // O^T += V^T . P^T for sub-block h of stage s: 16 MFMAs.
+  auto pv = [&](int s, int h, const bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb][0] = f32x16{};
-      s[mb][1] = f32x16{};
-      const uint16_t* kr = &sm.k[buf][mb * 32 + kperm][hl * 8];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + kk * 16);
-        s[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][kk], s[mb][0], 0, 0, 0);
-        s[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][kk], s[mb][1], 0, 0, 0);
-      }
-    }
-
-    // online softmax (log2 domain)
-    const bool need_mask = kb + KB - 1 > p_min;
-    bf16x8 pb[2][4];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float t = s[mb][nb][v] * scale_log2;
-          if (need_mask) {
-            const int key = kb + 32 * mb + 16 * (v >> 3) + 8 * hl + (v & 7);
-            t = key > pos_q[nb] ? -INFINITY : t;
-          }
-          s[mb][nb][v] = t;
-          mx = fmaxf(mx, t);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[nb], mx);
-      const float alpha = exp2f(m_run[nb] - m_new);
-      m_run[nb] = m_new;
-      float ls = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int hv = 0; hv < 2; ++hv) {
-          float p[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            p[i] = exp2f(s[mb][nb][hv * 8 + i] - m_new);
-            ls += p[i];
-          }
-          u32x4 pk;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pk[i] = pack_bf2(p[2 * i], p[2 * i + 1]);
-          pb[nb][mb * 2 + hv] = __builtin_bit_cast(bf16x8, pk);
-        }
-      l_run[nb] = l_run[nb] * alpha + ls;
-      if (WITH_O) {
-#pragma unroll
-        for (int md = 0; md < 4; ++md) oacc[md][nb] *= alpha;
-      }
-    }
-
-    if (WITH_O) {
-      // O^T += V^T . P^T
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int md = 0; md < 4; ++md) {
-        const uint16_t* vr = &sm.v[buf][md * 32 + (lane & 31)][hl * 8];
+        const int d = md * 32 + (lane & 31);
+        const int half = hl ^ ((d >> 3) & 1);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&st[s].v[2 * h + ks][d][half * 8]);
+        oacc[md][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[0][ks], oacc[md][0], 0, 0, 0);
+        oacc[md][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[1][ks], oacc[md][1], 0, 0, 0);
+      }
+  };
+
+  // Softmax of one query half of a sub-block (keys kb .. kb+31): S -> P (bf16,
+  // B operand of PV).  The running max of the half is raised only when the
+  // sub-block exceeds it by more than 2^8 in the exp2 domain (alpha[nb] is
+  // then the O scale factor).  Returns true if O's half must be rescaled.
+  auto softmax_half = [&](f32x16& S, bool mask, int kb, int nb, bf16x8 (&P)[2]) __attribute__((always_inline)) {
+    if (mask) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vr + ks * 16);
-          oacc[md][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][ks], oacc[md][0], 0, 0, 0);
-          oacc[md][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][ks], oacc[md][1], 0, 0, 0);
+      for (int v = 0; v < 16; ++v) {
+        const int key = kb + 16 * (v >> 3) + 8 * hl + (v & 7);
+        S[v] = key > pos_q[nb] ? -INFINITY : S[v];
+      }
+    }
+    float a = S[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) a = fmaxf(a, S[v]);
+    const float mx = fmaxf(a, xhalf(a));
+    const bool any = __ballot((mx - m_run[nb]) * c > 8.f) != 0ull;
+    const float m_new = any ? fmaxf(m_run[nb], mx) : m_run[nb];
+    alpha[nb] = __builtin_amdgcn_exp2f((m_run[nb] - m_new) * c);
+    m_run[nb] = m_new;
+    const float mc = m_new * c;
+    float ls = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(fmaf(S[ks * 8 + i], c, -mc));
+        ls += p[i];
+      }
+      u32x4 pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[i] = pack_bf2(p[2 * i], p[2 * i + 1]);
+      P[ks] = __builtin_bit_cast(bf16x8, pk);
+    }
+    l_run[nb] = l_run[nb] * alpha[nb] + ls;
+    return any;
+  };
+  // O[:, nb] *= alpha[nb].  The empty volatile asm keeps this a real (rarely
+  // taken) branch: the compiler would otherwise speculate the 64 multiplies,
+  // which on AGPR accumulators cost 3 instructions each, into every step.
+  // The accumulators stay in AGPRs: the MFMAs read and write them there.
+  auto rescale_half = [&](int nb) __attribute__((always_inline)) {
+    // Done element by element inside AGPRs (read, multiply, write back) so
+    // that O never gets a VGPR copy the register allocator would have to
+    // keep.  The s_nops cover the MFMA-write -> accvgpr-read and
+    // accvgpr-write -> MFMA-read distances (this path is rare).
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4");
+#pragma unroll
+    for (int md = 0; md < 4; ++md)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float t;
+        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                     : "+a"(oacc[md][nb][v]), "=&v"(t) : "v"(alpha[nb]));
+      }
+    asm volatile("s_nop 4");
+  };
+
+  // One step: QK^T of the next sub-block (its K operand kf already loaded),
+  // its softmax half by half, and PV of the current sub-block (s, h) with P,
+  // in one straight-line block whose MFMAs and VALU work the scheduler
+  // interleaves (half 0's softmax under half 1's QK^T, half 1's softmax under
+  // PV).  The K operand of the sub-block after next (s_pf, h_pf) is
+  // prefetched into kf.  MASK is compile-time.
+  auto step = [&](auto mask_tag, bf16x8 (&kf)[8], int kb_next, int s, int h,
+                  const bf16x8 (&P)[2][2], bf16x8 (&Pn)[2][2], int s_pf, int h_pf,
+                  bool do_pv) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 S0, S1;
+    qk_half(kf, 0, S0);
+    qk_half(kf, 1, S1);
+    load_k(s_pf, h_pf, kf);
+    const bool r0 = softmax_half(S0, MASK, kb_next, 0, Pn[0]);
+    if (WITH_O && do_pv) pv(s, h, P);
+    const bool r1 = softmax_half(S1, MASK, kb_next, 1, Pn[1]);
+    asm volatile("" : "+v"(Pn[0][0]), "+v"(Pn[0][1]), "+v"(Pn[1][0]), "+v"(Pn[1][1]));
+    // 8 QK^T MFMAs of half 0, then one MFMA per group of VALU work
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if (WITH_O && r0) rescale_half(0);
+    if (WITH_O && r1) rescale_half(1);
+  };
+
+  const int n_sub = (k1 - k0 + 31) / 32;
+  const int n_stage = (n_sub + 1) / 2;
+  const bool tail_partial = k0 + n_stage * KB - 1 > kmax;   // last stage holds keys past kmax
+  // prologue: stages 0 and 1 in flight; softmax of sub-block 0; K of sub-block 1
+  issue_stage(k0, 0);
+  if (n_stage > 1) issue_stage(k0 + KB, 1);
+  __syncthreads();                          // waits for this wave's loads, then all waves
+  bf16x8 kf[8];
+  bf16x8 Pa[2][2], Pb[2][2];
+  {
+    load_k(0, 0, kf);
+    f32x16 S0, S1;
+    qk_half(kf, 0, S0);
+    qk_half(kf, 1, S1);
+    const bool mask0 = k0 + 31 > wave_pmin;
+    if (softmax_half(S0, mask0, k0, 0, Pa[0]) && WITH_O) rescale_half(0);
+    if (softmax_half(S1, mask0, k0, 1, Pa[1]) && WITH_O) rescale_half(1);
+    load_k(0, 1, kf);
+  }
+
+  // Iteration b: barrier (stage b+1 resident, stage b-1 free), issue stage
+  // b+2, then step A (softmax of sub-block 2b+1, PV of 2b) and step B
+  // (softmax of 2b+2 from stage b+1, PV of 2b+1).  Sub-blocks wholly below
+  // the tile's first query row need no causal mask: for b < b_plain both
+  // steps are unmasked.  The last stage is peeled.
+  const int tile_pmin = it.pad0;
+  const int n_plain_sub = max(0, (tile_pmin - k0 + 1) / 32);
+  const int b_plain = min(n_stage - 1, max(0, (n_plain_sub - 1) / 2));
+  auto iteration = [&](auto mask_tag, int b) __attribute__((always_inline)) {
+    const int s = b % NSTAGE, s1 = (b + 1) % NSTAGE;
+    const int kb = k0 + b * KB;
+    __syncthreads();
+    if (b + 2 < n_stage) issue_stage(kb + 2 * KB, (b + 2) % NSTAGE);
+    step(mask_tag, kf, kb + 32, s, 0, Pa, Pb, s1, 0, true);
+    step(mask_tag, kf, kb + KB, s, 1, Pb, Pa, s1, 1, true);
+  };
+  int b = 0;
+  for (; b < b_plain; ++b) iteration(std::false_type{}, b);
+  for (; b + 1 < n_stage; ++b) iteration(std::true_type{}, b);
+  {
+    const int s = b % NSTAGE;
+    __syncthreads();
+    if (tail_partial) {                     // no wave has read this stage's V yet
+      zero_tail(k0 + b * KB, s);
+      __syncthreads();
+    }
+    if (2 * b + 1 < n_sub) {
+      step(std::true_type{}, kf, k0 + b * KB + 32, s, 0, Pa, Pb, s, 1, true);
+      if (WITH_O) pv(s, 1, Pb);
+    } else if (WITH_O) {
+      pv(s, 0, Pa);
+    }
+  }
+
+  // ---- epilogue ----------------------------------------------------------------
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int p = 64 * w + 32 * nb + (lane & 31);
+    const bool valid = p < npairs;
+    const int r = p / G, hh = p - r * G;
+    const int m = it.row0 + r;
+    const int h = g * G + hh;
+    const float l_tot = l_run[nb] + xhalf(l_run[nb]);
+    const float m2 = m_run[nb] * c;                     // log2-domain max
+    if (it.slot < 0) {
+      if (lse && valid && hl == 0) lse[(size_t)m * hq + h] = (m2 + __log2f(l_tot)) * kLn2;
+      if (WITH_O && valid) {
+        const float inv = 1.f / l_tot;
+        uint16_t* op = o + ((size_t)m * hq + h) * 128 + 4 * hl;
+#pragma unroll
+        for (int md = 0; md < 4; ++md)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            u32x2 pk;
+            pk[0] = pack_bf2(oacc[md][nb][4 * j] * inv, oacc[md][nb][4 * j + 1] * inv);
+            pk[1] = pack_bf2(oacc[md][nb][4 * j + 2] * inv, oacc[md][nb][4 * j + 3] * inv);
+            *reinterpret_cast<u32x2*>(op + md * 32 + 8 * j) = pk;
+          }
+      }
+    } else if (it.slot < max_slots) {
+      const size_t pslot = ((size_t)it.slot * hkv + g) * PAIRS + p;
+      if (hl == 0) {
+        part_ml[2 * pslot] = m2;
+        part_ml[2 * pslot + 1] = l_tot;
+      }
+      if (WITH_O) {                        // normalised partial output, fp32
+        const float inv = 1.f / l_tot;
+        float* op = part_o + pslot * 128 + 4 * hl;
+#pragma unroll
+        for (int md = 0; md < 4; ++md)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            f32x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = oacc[md][nb][4 * j + e] * inv;
+            *reinterpret_cast<f32x4*>(op + md * 32 + 8 * j) = v4;
+          }
+      }
+    }
+  }
+}
+
+// Combines the key chunks of split tiles (chunk order fixed):
+//   M = max_c m_c,  w_c = l_c 2^(m_c - M),  O = sum_c w_c O_c / sum_c w_c,
+//   LSE = (M + log2 sum_c w_c) ln 2.
+// One workgroup per (merge tile, kv head); 16 threads per pair, 8 head
+// dimensions per thread.
+template <bool WITH_O>
+__global__ __launch_bounds__(256) void attn_merge(
+    const MergeTile* __restrict__ merges, const int32_t* __restrict__ counters, int hkv, int G,
+    const float* __restrict__ part_ml, const float* __restrict__ part_o,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int max_slots) {
+  const int g = blockIdx.x % hkv;
+  const int mi = blockIdx.x / hkv;
+  if (mi >= counters[1]) return;
+  const MergeTile mt = merges[mi];
+  if (mt.slot0 < 0 || mt.slot0 + mt.n_chunks > max_slots) return;
+  const int hq = G * hkv;
+  const int npairs = mt.nrows * G;
+  const int sub = threadIdx.x & 15;
+  for (int p = threadIdx.x >> 4; p < npairs; p += 16) {
+    float M = -INFINITY;
+    for (int c = 0; c < mt.n_chunks; ++c) {
+      const size_t ps = ((size_t)(mt.slot0 + c) * hkv + g) * PAIRS + p;
+      M = fmaxf(M, part_ml[2 * ps]);
+    }
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float wsum = 0.f;
+    for (int c = 0; c < mt.n_chunks; ++c) {
+      const size_t ps = ((size_t)(mt.slot0 + c) * hkv + g) * PAIRS + p;
+      const float wc = part_ml[2 * ps + 1] * __builtin_amdgcn_exp2f(part_ml[2 * ps] - M);
+      wsum += wc;
+      if (WITH_O) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(part_o + ps * 128 + sub * 8);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(part_o + ps * 128 + sub * 8 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] = fmaf(wc, a0[e], acc[e]);
+          acc[4 + e] = fmaf(wc, a1[e], acc[4 + e]);
         }
       }
     }
-    if (b + 1 < n_blk) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue --------------------------------------------------------------
+    const int r = p / G, hh = p - r * G;
+    const int m = mt.row0 + r;
+    const int h = g * G + hh;
+    if (lse && sub == 0) lse[(size_t)m * hq + h] = (M + __log2f(wsum)) * kLn2;
+    if (WITH_O) {
+      const float inv = 1.f / wsum;
+      u32x4 pk;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int qi = (lane & 31) + 32 * nb;
-    const bool valid = qi < tl.nrows;
-    const float l_tot = l_run[nb] + __shfl_xor(l_run[nb], 32);
-    const int m = tl.row0 + qi;
-    if (lse && valid && hl == 0) lse[(size_t)m * hq + h] = (m_run[nb] + __log2f(l_tot)) * kLn2;
-    if (WITH_O && valid) {
-      const float inv = 1.f / l_tot;
-      uint16_t* op = o + ((size_t)m * hq + h) * 128 + 4 * hl;
-#pragma unroll
-      for (int md = 0; md < 4; ++md)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x2 pk;
-          pk[0] = pack_bf2(oacc[md][nb][4 * j] * inv, oacc[md][nb][4 * j + 1] * inv);
-          pk[1] = pack_bf2(oacc[md][nb][4 * j + 2] * inv, oacc[md][nb][4 * j + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + md * 32 + 8 * j) = pk;
-        }
+      for (int e = 0; e < 4; ++e) pk[e] = pack_bf2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+      *reinterpret_cast<u32x4*>(o + ((size_t)m * hq + h) * 128 + sub * 8) = pk;
     }
   }
 }
@@ -355,39 +750,48 @@ __global__ __launch_bounds__(64) void attn_rows_f32(
   if (lse && lane == 0) lse[(size_t)m * hq + h] = m_run + logf(l_run);
 }
 
-template <int G, bool WITH_O>
-sx_status launch_attn_bf16(int grid, const void* q, const int32_t* q_index, const int32_t* rows,
-                      const sx_layout& lay, const sx_pages& kv, int hkv, void* o, float* lse,
-                      const AttnTile* tiles, const int* n_tiles, float scale_log2,
-                      hipStream_t stream) {
-  const size_t smem = sizeof(AttnSmem<G>);
-  const sx_status st = allow_lds((const void*)attn_bf16<G, WITH_O>, smem, "attention");
-  if (st != SX_OK) return st;
-  attn_bf16<G, WITH_O><<<grid, G * 64, smem, stream>>>(
-      (const uint16_t*)q, q_index, rows, lay, kv.n_pages, (const uint16_t*)kv.k,
-      (const uint16_t*)kv.v, hkv, (uint16_t*)o, lse, tiles, n_tiles, scale_log2);
-  return SX_OK;
-}
-
 template <bool WITH_O>
-sx_status dispatch_g(int G, int grid, const void* q, const int32_t* q_index, const int32_t* rows,
-                     const sx_layout& lay, const sx_pages& kv, int hkv, void* o, float* lse,
-                     const AttnTile* tiles, const int* n_tiles, float scale_log2, hipStream_t s) {
-  switch (G) {
-    case 1: return launch_attn_bf16<1, WITH_O>(grid, q, q_index, rows, lay, kv, hkv, o, lse, tiles, n_tiles, scale_log2, s);
-    case 2: return launch_attn_bf16<2, WITH_O>(grid, q, q_index, rows, lay, kv, hkv, o, lse, tiles, n_tiles, scale_log2, s);
-    case 4: return launch_attn_bf16<4, WITH_O>(grid, q, q_index, rows, lay, kv, hkv, o, lse, tiles, n_tiles, scale_log2, s);
-    case 7: return launch_attn_bf16<7, WITH_O>(grid, q, q_index, rows, lay, kv, hkv, o, lse, tiles, n_tiles, scale_log2, s);
-    case 8: return launch_attn_bf16<8, WITH_O>(grid, q, q_index, rows, lay, kv, hkv, o, lse, tiles, n_tiles, scale_log2, s);
-    default: return set_error(SX_EUNSUPPORTED, "bf16 attention: n_q_heads/n_kv_heads = %d not built (1,2,4,7,8)", G);
-  }
+sx_status launch_bf16(const sx_dims& dims, const sx_layout& lay, const void* q,
+                      const int32_t* q_index, const int32_t* rows, const int32_t* row_start,
+                      int n_rows, const sx_pages& kv, void* o, float* lse, void* ws,
+                      hipStream_t stream) {
+  const int hq = dims.n_q_heads, hkv = dims.n_kv_heads, G = hq / hkv;
+  const WsLayout L = ws_layout(n_rows, lay.n_req, G, hkv, WITH_O);
+  char* base = static_cast<char*>(ws);
+  int32_t* counters = reinterpret_cast<int32_t*>(base + L.counters);
+  TileInfo* tiles = reinterpret_cast<TileInfo*>(base + L.tiles);
+  AttnItem* items = reinterpret_cast<AttnItem*>(base + L.items);
+  MergeTile* merges = reinterpret_cast<MergeTile*>(base + L.merges);
+  float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
+  float* part_o = WITH_O ? reinterpret_cast<float*>(base + L.part_o) : nullptr;
+  const int M = rows_per_tile(G);
+  const int target = items_per_head(hkv);
+  build_work<<<1, kBuildThreads, (size_t)(lay.n_req + 1) * sizeof(int), stream>>>(row_start, rows, lay.seq_start, lay.n_req, n_rows, M,
+                                              target, L.max_tiles, L.max_items, 1, tiles, items,
+                                              merges, counters);
+  sx_status st = check_launch("attention work list");
+  if (st != SX_OK) return st;
+  const size_t smem = NSTAGE * sizeof(Stage);
+  st = allow_lds((const void*)attn_fwd<WITH_O>, smem, "attention");
+  if (st != SX_OK) return st;
+  const float scale_log2 = kLog2e / sqrtf((float)dims.head_dim);
+  attn_fwd<WITH_O><<<L.max_items * hkv, 256, smem, stream>>>(
+      (const uint16_t*)q, q_index, rows, lay, kv.n_pages, (const uint16_t*)kv.k,
+      (const uint16_t*)kv.v, hkv, G, (uint16_t*)o, lse, items, counters, part_ml, part_o,
+      L.max_items, scale_log2);
+  st = check_launch("attention");
+  if (st != SX_OK) return st;
+  attn_merge<WITH_O><<<L.max_tiles * hkv, 256, 0, stream>>>(merges, counters, hkv, G, part_ml,
+                                                           part_o, (uint16_t*)o, lse, L.max_items);
+  return check_launch("attention merge");
 }
 
 }  // namespace
 
-size_t attn_ws_bytes(int n_rows, int n_req) {
-  const size_t max_tiles = (size_t)(n_rows + kTileRows - 1) / kTileRows + (size_t)n_req;
-  return align256(sizeof(int)) + align256(max_tiles * sizeof(AttnTile));
+size_t attn_ws_bytes(const sx_dims& dims, int n_rows, int n_req, bool with_o) {
+  if (dims.dtype != SX_BF16 || n_rows <= 0) return 0;
+  const int G = dims.n_q_heads / dims.n_kv_heads;
+  return ws_layout(n_rows, n_req, G, dims.n_kv_heads, with_o).total;
 }
 
 sx_status launch_attention(const sx_dims& dims, const sx_layout& lay, const void* q,
@@ -409,20 +813,8 @@ sx_status launch_attention(const sx_dims& dims, const sx_layout& lay, const void
                                                   hkv, hq, (float*)o, lse, scale);
     return check_launch("attention (fp32)");
   }
-  int* n_tiles = reinterpret_cast<int*>(ws);
-  AttnTile* tiles = reinterpret_cast<AttnTile*>(static_cast<char*>(ws) + align256(sizeof(int)));
-  const int max_tiles = (n_rows + kTileRows - 1) / kTileRows + lay.n_req;
-  build_tiles<<<1, 256, (size_t)lay.n_req * sizeof(int), stream>>>(row_start, lay.n_req, n_rows,
-                                                                    max_tiles, tiles, n_tiles);
-  sx_status st = check_launch("attention tile table");
-  if (st != SX_OK) return st;
-  const int G = hq / hkv;
-  const float scale_log2 = kLog2e / sqrtf((float)d);
-  const int grid = max_tiles * hkv;
-  st = o ? dispatch_g<true>(G, grid, q, q_index, rows, lay, kv, hkv, o, lse, tiles, n_tiles, scale_log2, stream)
-         : dispatch_g<false>(G, grid, q, q_index, rows, lay, kv, hkv, o, lse, tiles, n_tiles, scale_log2, stream);
-  if (st != SX_OK) return st;
-  return check_launch("attention");
+  return o ? launch_bf16<true>(dims, lay, q, q_index, rows, row_start, n_rows, kv, o, lse, ws, stream)
+           : launch_bf16<false>(dims, lay, q, q_index, rows, row_start, n_rows, kv, o, lse, ws, stream);
 }
 
 }  // namespace sx

@@ -333,7 +333,7 @@ size_t select_ws_bytes(const sx_dims& d, int n_tok, int n_sq, int n_req) {
   return align256((size_t)d.n_kv_heads * n_tok * sizeof(float))   // partial scores
          + align256((size_t)n_tok * sizeof(float))                // scores if caller passes none
          + align256((size_t)n_sq * d.n_q_heads * sizeof(float))   // probe LSE
-         + attn_ws_bytes(n_sq, n_req);                             // probe tile table
+         + attn_ws_bytes(d, n_sq, n_req, false);                   // probe work list
 }
 
 sx_status launch_scores(const sx_dims& dims, const sx_layout& lay, const void* q,

@@ -28,8 +28,13 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Two floats -> two bf16 (RNE) in one 32-bit word, lo in bits 0-15
+// (a single v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t r = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // Request owning packed token `tok` (seq_start ascending, n_req+1 entries).

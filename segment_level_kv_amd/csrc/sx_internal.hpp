@@ -18,18 +18,11 @@ sx_status check_launch(const char* what);
 // Lets `kernel` use `bytes` of dynamic LDS (gfx950 has 160 KB per CU).
 sx_status allow_lds(const void* kernel, size_t bytes, const char* what);
 
-// Attention query tile: 64 consecutive active rows of one request.
-constexpr int kTileRows = 64;
-struct AttnTile {
-  int32_t req;
-  int32_t row0;     // first row (index into the row list)
-  int32_t nrows;    // 1..kTileRows
-  int32_t pad;
-};
-
 // Workspace carving (all offsets 256-byte aligned).
 size_t align256(size_t x);
-size_t attn_ws_bytes(int n_rows, int n_req);
+// Attention workspace (bf16 path): work list and partial results of key
+// chunks; 0 for fp32.  with_o false: log-sum-exp only (no partial outputs).
+size_t attn_ws_bytes(const sx_dims& d, int n_rows, int n_req, bool with_o);
 size_t topk_ws_bytes(int n_tok, int n_req);
 size_t select_ws_bytes(const sx_dims& d, int n_tok, int n_sq, int n_req);
 

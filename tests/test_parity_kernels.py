@@ -358,3 +358,46 @@ def test_topk_bit_exact_adversarial():
         ref = oracle.select_topk(sc, cand, ks[r])
         assert np.array_equal(got[off:off + ks[r]] - seq[r], ref), f"request {r}"
         off += ks[r]
+
+
+@pytest.mark.parametrize("shape", ["llama", "qwen"])
+def test_sparse_attention_many_chunks_and_nan_tail(shape):
+    """Long requests with few active rows: every query tile is split into
+    many key chunks (merged afterwards); the slots past each request's last
+    token hold NaN, which must never reach the output."""
+    dims = SHAPES[shape]
+    lens = [9000, 2100]
+    say(f"[attn chunks] shape={shape} lens={lens}")
+    rng, seq, pool, kh, vh, bt = _attn_inputs(dims, lens, 71)
+    # poison the unused slots of each request's last page (K and V)
+    for r, n in enumerate(lens):
+        if n % 16:
+            pg = int(bt[r, n // 16])
+            pool.k[pg, :, n % 16:, :] = float("nan")
+            pool.v[pg, :, :, n % 16:] = float("nan")
+    rows, starts = [], [0]
+    for r, n in enumerate(lens):
+        sel = np.flatnonzero(rng.random(n) < 0.03)
+        sel = np.union1d(sel, [0, n - 1])
+        rows.append(sel + seq[r])
+        starts.append(starts[-1] + len(sel))
+    rows = np.concatenate(rows).astype(np.int32)
+    n_rows = len(rows)
+    q = _store(rng.standard_normal((n_rows, dims.n_q_heads, dims.head_dim)) * 1.5, dims)
+    dt = LY.storage_dtype(dims.dtype)
+    lay = LY.DeviceLayout(seq, bt, LY.rope_table(dims.theta, dims.head_dim, 16, DEV), DEV)
+    cd = LY.make_dims(dims)
+    o = torch.zeros((n_rows, dims.n_q_heads * dims.head_dim), dtype=dt, device=DEV)
+    lse = torch.zeros((n_rows, dims.n_q_heads), dtype=torch.float32, device=DEV)
+    ws = LY.workspace(L.SX_OP_SPARSE_ATTN, cd, int(seq[-1]), n_rows, len(lens), DEV)
+    L.sx_sparse_attn(cd, lay.struct, torch.from_numpy(q).to(dt).to(DEV), torch.from_numpy(rows).to(DEV),
+                     torch.from_numpy(np.array(starts, np.int32)).to(DEV), n_rows, pool.struct(), o, lse, ws)
+    torch.cuda.synchronize()
+    og = o.float().cpu().double().numpy()
+    lg = lse.cpu().double().numpy()
+    for r in range(len(lens)):
+        K, V = _logical(kh, vh, bt[r], 0, lens[r])
+        sl = slice(starts[r], starts[r + 1])
+        ref, lref = oracle.causal_attention(q[sl], rows[sl] - seq[r], K, V)
+        assert_close_bf16(og[sl], ref.reshape(len(ref), -1), what=f"O req {r}")
+        assert np.max(np.abs(lg[sl] - lref)) < 2e-3
