@@ -297,7 +297,16 @@ __global__ __launch_bounds__(kBuildThreads) void build_work(
   }
 }
 
-__device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32); }
+// max / sum of a value over the two lane halves (lanes l and l^32), in every
+// lane: v_permlane32_swap exchanges the halves without going through LDS.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <bool WITH_O>
 __global__ __launch_bounds__(256, 1) void attn_fwd(
@@ -374,23 +383,43 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
     voff[i] = (uint32_t)(d * 16 + (((lane & 1) ^ ((d >> 3) & 1)) * 8)) * 2u;
   }
   const size_t head_bytes = (size_t)kPage * 128 * 2;      // one page-head, 4 KB
-  auto issue_stage = [&](int kb, int s) __attribute__((always_inline)) {
-    int pi = min(kb / kPage + w, last_pi);
-    int pg = bt[pi];
-    pg = (pg >= 0 && pg < n_pages) ? pg : 0;
+  // Page id of this wave's page of the block at kb (scalar load: the wave
+  // index is made wave-uniform).  Fetched one stage ahead of its use, so the
+  // load latency is not paid when the copies are issued.
+  // The block table is read-only for the whole kernel, so it is read through
+  // the constant address space: a scalar load (s_load, counted by lgkmcnt)
+  // rather than a vector load whose vmcnt wait would also wait for the
+  // stage copies in flight.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  typedef __attribute__((address_space(4))) const int32_t* cptr_t;
+  const cptr_t btc = (cptr_t)bt;
+  auto page_of_block = [&](int kb) __attribute__((always_inline)) {
+    const int pi = min(kb / kPage + wu, last_pi);
+    const int pg = btc[pi];
+    return (pg >= 0 && pg < n_pages) ? pg : 0;
+  };
+  // The K and V halves of a stage are issued separately (at different points
+  // of an iteration) so that a wave never queues all its copies at once.
+  auto issue_k = [&](int pg, int s) __attribute__((always_inline)) {
     const size_t base = ((size_t)pg * hkv + g) * head_bytes;
     const unsigned char* kp = reinterpret_cast<const unsigned char*>(kpool) + base;
-    unsigned char* kst = reinterpret_cast<unsigned char*>(&st[s].k[16 * w][0]);
+    unsigned char* kst = reinterpret_cast<unsigned char*>(&st[s].k[16 * wu][0]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_global_load_lds((gptr_t)(kp + koff[i]), (lptr_t)(kst + i * 1024), 16, 0, 0);
-    if (WITH_O) {
-      const unsigned char* vp = reinterpret_cast<const unsigned char*>(vpool) + base;
-      unsigned char* vst = reinterpret_cast<unsigned char*>(&st[s].v[w][0][0]);
+  };
+  auto issue_v = [&](int pg, int s) __attribute__((always_inline)) {
+    if (!WITH_O) return;
+    const size_t base = ((size_t)pg * hkv + g) * head_bytes;
+    const unsigned char* vp = reinterpret_cast<const unsigned char*>(vpool) + base;
+    unsigned char* vst = reinterpret_cast<unsigned char*>(&st[s].v[wu][0][0]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds((gptr_t)(vp + voff[i]), (lptr_t)(vst + i * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(vp + voff[i]), (lptr_t)(vst + i * 1024), 16, 0, 0);
+  };
+  auto issue_stage = [&](int pg, int s) __attribute__((always_inline)) {
+    issue_k(pg, s);
+    issue_v(pg, s);
   };
   // Zero the values of keys past kmax in a resident stage (P is 0 there, but
   // those slots may hold anything, and 0 * NaN would poison O).
@@ -440,18 +469,32 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   float alpha[2] = {1.f, 1.f};
   const float c = scale_log2;
 
-  // O^T += V^T . P^T for sub-block h of stage s: 16 MFMAs.
-  auto pv = [&](int s, int h, const bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
+  // V^T operand of sub-block h of stage s: 8 x 16 B (all loaded before the
+  // MFMAs that use them, so LDS latency is not paid per MFMA pair).
+  auto load_v = [&](int s, int h, bf16x8 (&vf)[8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int md = 0; md < 4; ++md) {
         const int d = md * 32 + (lane & 31);
         const int half = hl ^ ((d >> 3) & 1);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&st[s].v[2 * h + ks][d][half * 8]);
-        oacc[md][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[0][ks], oacc[md][0], 0, 0, 0);
-        oacc[md][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[1][ks], oacc[md][1], 0, 0, 0);
+        vf[ks * 4 + md] = *reinterpret_cast<const bf16x8*>(&st[s].v[2 * h + ks][d][half * 8]);
       }
+  };
+  // O^T += V^T . P^T for one sub-block: 16 MFMAs.
+  auto pv_mfma = [&](const bf16x8 (&vf)[8], const bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int md = 0; md < 4; ++md) {
+        oacc[md][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks * 4 + md], P[0][ks], oacc[md][0], 0, 0, 0);
+        oacc[md][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks * 4 + md], P[1][ks], oacc[md][1], 0, 0, 0);
+      }
+  };
+  auto pv = [&](int s, int h, const bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
+    bf16x8 vf[8];
+    load_v(s, h, vf);
+    pv_mfma(vf, P);
   };
 
   // Softmax of one query half of a sub-block (keys kb .. kb+31): S -> P (bf16,
@@ -466,30 +509,33 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
         S[v] = key > pos_q[nb] ? -INFINITY : S[v];
       }
     }
-    float a = S[0];
+    // tree of 3-input maxima (8 v_max3, depth 3)
+    float t[5];
 #pragma unroll
-    for (int v = 1; v < 16; ++v) a = fmaxf(a, S[v]);
-    const float mx = fmaxf(a, xhalf(a));
+    for (int i = 0; i < 5; ++i) t[i] = fmaxf(fmaxf(S[3 * i], S[3 * i + 1]), S[3 * i + 2]);
+    const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]);
+    const float u1 = fmaxf(fmaxf(t[3], t[4]), S[15]);
+    const float mx = half_max(fmaxf(u0, u1));
     const bool any = __ballot((mx - m_run[nb]) * c > 8.f) != 0ull;
     const float m_new = any ? fmaxf(m_run[nb], mx) : m_run[nb];
     alpha[nb] = __builtin_amdgcn_exp2f((m_run[nb] - m_new) * c);
     m_run[nb] = m_new;
     const float mc = m_new * c;
-    float ls = 0.f;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};      // four partial sums: short chains
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         p[i] = __builtin_amdgcn_exp2f(fmaf(S[ks * 8 + i], c, -mc));
-        ls += p[i];
+        ls[i & 3] += p[i];
       }
       u32x4 pk;
 #pragma unroll
       for (int i = 0; i < 4; ++i) pk[i] = pack_bf2(p[2 * i], p[2 * i + 1]);
       P[ks] = __builtin_bit_cast(bf16x8, pk);
     }
-    l_run[nb] = l_run[nb] * alpha[nb] + ls;
+    l_run[nb] = l_run[nb] * alpha[nb] + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
     return any;
   };
   // O[:, nb] *= alpha[nb].  The empty volatile asm keeps this a real (rarely
@@ -513,32 +559,27 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
     asm volatile("s_nop 4");
   };
 
-  // One step: QK^T of the next sub-block (its K operand kf already loaded),
-  // its softmax half by half, and PV of the current sub-block (s, h) with P,
-  // in one straight-line block whose MFMAs and VALU work the scheduler
-  // interleaves (half 0's softmax under half 1's QK^T, half 1's softmax under
-  // PV).  The K operand of the sub-block after next (s_pf, h_pf) is
-  // prefetched into kf.  MASK is compile-time.
-  auto step = [&](auto mask_tag, bf16x8 (&kf)[8], int kb_next, int s, int h,
-                  const bf16x8 (&P)[2][2], bf16x8 (&Pn)[2][2], int s_pf, int h_pf,
-                  bool do_pv) __attribute__((always_inline)) {
+  // One step j of a three-stage pipeline over 32-key sub-blocks: QK^T of
+  // sub-block j+2 (into Sn), PV of sub-block j (with P), softmax of
+  // sub-block j+1 (Sc -> Pn).  The three are independent, so the scheduler
+  // can place the softmax VALU work between all 32 MFMAs of the step.  O is
+  // rescaled at the end of the step (after PV j, before PV j+1) if the
+  // softmax raised a running max.  MASK is compile-time.
+  auto step = [&](auto mask_tag, bool do_qk, int s_q, int h_q, int s_v, int h_v,
+                  f32x16 (&Sc)[2], f32x16 (&Sn)[2], int kb_soft, const bf16x8 (&P)[2][2],
+                  bf16x8 (&Pn)[2][2]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    f32x16 S0, S1;
-    qk_half(kf, 0, S0);
-    qk_half(kf, 1, S1);
-    load_k(s_pf, h_pf, kf);
-    const bool r0 = softmax_half(S0, MASK, kb_next, 0, Pn[0]);
-    if (WITH_O && do_pv) pv(s, h, P);
-    const bool r1 = softmax_half(S1, MASK, kb_next, 1, Pn[1]);
-    asm volatile("" : "+v"(Pn[0][0]), "+v"(Pn[0][1]), "+v"(Pn[1][0]), "+v"(Pn[1][1]));
-    // 8 QK^T MFMAs of half 0, then one MFMA per group of VALU work
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 24; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    bf16x8 kf[8], vf[8];
+    if (do_qk) load_k(s_q, h_q, kf);
+    if (WITH_O) load_v(s_v, h_v, vf);
+    if (do_qk) {
+      qk_half(kf, 0, Sn[0]);
+      qk_half(kf, 1, Sn[1]);
     }
+    if (WITH_O) pv_mfma(vf, P);
+    const bool r0 = softmax_half(Sc[0], MASK, kb_soft, 0, Pn[0]);
+    const bool r1 = softmax_half(Sc[1], MASK, kb_soft, 1, Pn[1]);
+    asm volatile("" : "+v"(Pn[0][0]), "+v"(Pn[0][1]), "+v"(Pn[1][0]), "+v"(Pn[1][1]));
     if (WITH_O && r0) rescale_half(0);
     if (WITH_O && r1) rescale_half(1);
   };
@@ -546,28 +587,34 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   const int n_sub = (k1 - k0 + 31) / 32;
   const int n_stage = (n_sub + 1) / 2;
   const bool tail_partial = k0 + n_stage * KB - 1 > kmax;   // last stage holds keys past kmax
-  // prologue: stages 0 and 1 in flight; softmax of sub-block 0; K of sub-block 1
-  issue_stage(k0, 0);
-  if (n_stage > 1) issue_stage(k0 + KB, 1);
+  // prologue: stages 0 and 1 in flight; S of sub-blocks 0 (even) and 1
+  // (odd); softmax of sub-block 0
+  issue_stage(page_of_block(k0), 0);
+  if (n_stage > 1) issue_stage(page_of_block(k0 + KB), 1);
+  int pg_next = page_of_block(k0 + 2 * KB);   // for stage 2
   __syncthreads();                          // waits for this wave's loads, then all waves
-  bf16x8 kf[8];
+  f32x16 S_even[2], S_odd[2];
   bf16x8 Pa[2][2], Pb[2][2];
   {
+    bf16x8 kf[8];
     load_k(0, 0, kf);
-    f32x16 S0, S1;
-    qk_half(kf, 0, S0);
-    qk_half(kf, 1, S1);
-    const bool mask0 = k0 + 31 > wave_pmin;
-    if (softmax_half(S0, mask0, k0, 0, Pa[0]) && WITH_O) rescale_half(0);
-    if (softmax_half(S1, mask0, k0, 1, Pa[1]) && WITH_O) rescale_half(1);
+    qk_half(kf, 0, S_even[0]);
+    qk_half(kf, 1, S_even[1]);
     load_k(0, 1, kf);
+    qk_half(kf, 0, S_odd[0]);
+    qk_half(kf, 1, S_odd[1]);
+    const bool mask0 = k0 + 31 > wave_pmin;
+    if (softmax_half(S_even[0], mask0, k0, 0, Pa[0]) && WITH_O) rescale_half(0);
+    if (softmax_half(S_even[1], mask0, k0, 1, Pa[1]) && WITH_O) rescale_half(1);
   }
 
   // Iteration b: barrier (stage b+1 resident, stage b-1 free), issue stage
-  // b+2, then step A (softmax of sub-block 2b+1, PV of 2b) and step B
-  // (softmax of 2b+2 from stage b+1, PV of 2b+1).  Sub-blocks wholly below
-  // the tile's first query row need no causal mask: for b < b_plain both
-  // steps are unmasked.  The last stage is peeled.
+  // b+2 (K before step A, V before step B), then
+  //   step A: QK^T 2b+2 (stage b+1), PV 2b (stage b), softmax 2b+1;
+  //   step B: QK^T 2b+3 (stage b+1), PV 2b+1 (stage b), softmax 2b+2.
+  // Sub-blocks wholly below the tile's first query row need no causal
+  // mask: for b < b_plain both softmaxes are unmasked.  The last stage is
+  // peeled.
   const int tile_pmin = it.pad0;
   const int n_plain_sub = max(0, (tile_pmin - k0 + 1) / 32);
   const int b_plain = min(n_stage - 1, max(0, (n_plain_sub - 1) / 2));
@@ -575,9 +622,13 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
     const int s = b % NSTAGE, s1 = (b + 1) % NSTAGE;
     const int kb = k0 + b * KB;
     __syncthreads();
-    if (b + 2 < n_stage) issue_stage(kb + 2 * KB, (b + 2) % NSTAGE);
-    step(mask_tag, kf, kb + 32, s, 0, Pa, Pb, s1, 0, true);
-    step(mask_tag, kf, kb + KB, s, 1, Pb, Pa, s1, 1, true);
+    const bool more = b + 2 < n_stage;
+    const int pg = pg_next;
+    if (more) issue_k(pg, (b + 2) % NSTAGE);
+    pg_next = page_of_block(kb + 3 * KB);
+    step(mask_tag, true, s1, 0, s, 0, S_odd, S_even, kb + 32, Pa, Pb);
+    if (more) issue_v(pg, (b + 2) % NSTAGE);
+    step(mask_tag, true, s1, 1, s, 1, S_even, S_odd, kb + KB, Pb, Pa);
   };
   int b = 0;
   for (; b < b_plain; ++b) iteration(std::false_type{}, b);
@@ -590,7 +641,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
       __syncthreads();
     }
     if (2 * b + 1 < n_sub) {
-      step(std::true_type{}, kf, k0 + b * KB + 32, s, 0, Pa, Pb, s, 1, true);
+      step(std::true_type{}, false, s, 0, s, 0, S_odd, S_even, k0 + b * KB + 32, Pa, Pb);
       if (WITH_O) pv(s, 1, Pb);
     } else if (WITH_O) {
       pv(s, 0, Pa);
@@ -605,7 +656,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
     const int r = p / G, hh = p - r * G;
     const int m = it.row0 + r;
     const int h = g * G + hh;
-    const float l_tot = l_run[nb] + xhalf(l_run[nb]);
+    const float l_tot = half_sum(l_run[nb]);
     const float m2 = m_run[nb] * c;                     // log2-domain max
     if (it.slot < 0) {
       if (lse && valid && hl == 0) lse[(size_t)m * hq + h] = (m2 + __log2f(l_tot)) * kLn2;
