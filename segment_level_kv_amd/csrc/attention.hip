@@ -41,7 +41,7 @@ namespace sx {
 namespace {
 
 constexpr int KB = 64;                 // keys per block
-constexpr int NSTAGE = 3;              // LDS ring depth
+constexpr int NSTAGE = 4;              // LDS ring depth (copies issued 2 stages ahead)
 constexpr int PAIRS = 256;             // (row, head) pairs per workgroup
 constexpr int kTargetItems = 768;      // work items aimed for (about 3 per CU)
 constexpr int kMinChunk = 1024;        // shortest key chunk of a split tile
@@ -306,6 +306,19 @@ __device__ __forceinline__ float half_max(float x) {
 __device__ __forceinline__ float half_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// s_waitcnt with at most VM vector-memory operations of this wave still in
+// flight and no LDS / scalar operation pending, then the workgroup barrier.
+// The stage copies (global_load_lds) write LDS asynchronously and are
+// tracked only by vmcnt, which the barrier itself does not wait for.
+// Written as one asm block: the compiler's own fence for a barrier would
+// otherwise be merged into the wait and turn it into vmcnt(0).  The memory
+// clobber keeps LDS accesses on their side of the barrier.
+template <int VM>
+__device__ __forceinline__ void vm_wait_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
 template <bool WITH_O>
@@ -587,12 +600,21 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   const int n_sub = (k1 - k0 + 31) / 32;
   const int n_stage = (n_sub + 1) / 2;
   const bool tail_partial = k0 + n_stage * KB - 1 > kmax;   // last stage holds keys past kmax
-  // prologue: stages 0 and 1 in flight; S of sub-blocks 0 (even) and 1
-  // (odd); softmax of sub-block 0
+  // Waits until at most `pending` of this wave's stage copies (the newest
+  // ones) are in flight, then the barrier.  pending is 0, 1 or 2 stages.
+  constexpr int per_stage = WITH_O ? 8 : 4;   // copies per wave per stage
+  auto wait_barrier = [&](int pending_stages) __attribute__((always_inline)) {
+    if (pending_stages >= 2) vm_wait_barrier<2 * per_stage>();
+    else if (pending_stages == 1) vm_wait_barrier<per_stage>();
+    else vm_wait_barrier<0>();
+  };
+  // prologue: stages 0..2 in flight; S of sub-blocks 0 (even) and 1 (odd);
+  // softmax of sub-block 0
   issue_stage(page_of_block(k0), 0);
   if (n_stage > 1) issue_stage(page_of_block(k0 + KB), 1);
-  int pg_next = page_of_block(k0 + 2 * KB);   // for stage 2
-  __syncthreads();                          // waits for this wave's loads, then all waves
+  if (n_stage > 2) issue_stage(page_of_block(k0 + 2 * KB), 2);
+  int pg_next = page_of_block(k0 + 3 * KB);   // for stage 3
+  wait_barrier(min(n_stage, 3) - 1);         // stage 0 resident in every wave
   f32x16 S_even[2], S_odd[2];
   bf16x8 Pa[2][2], Pb[2][2];
   {
@@ -608,8 +630,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
     if (softmax_half(S_even[1], mask0, k0, 1, Pa[1]) && WITH_O) rescale_half(1);
   }
 
-  // Iteration b: barrier (stage b+1 resident, stage b-1 free), issue stage
-  // b+2 (K before step A, V before step B), then
+  // Iteration b: wait + barrier (stage b+1 resident, stage b-1 free), issue
+  // stage b+3 (K before step A, V before step B), then
   //   step A: QK^T 2b+2 (stage b+1), PV 2b (stage b), softmax 2b+1;
   //   step B: QK^T 2b+3 (stage b+1), PV 2b+1 (stage b), softmax 2b+2.
   // Sub-blocks wholly below the tile's first query row need no causal
@@ -621,13 +643,13 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   auto iteration = [&](auto mask_tag, int b) __attribute__((always_inline)) {
     const int s = b % NSTAGE, s1 = (b + 1) % NSTAGE;
     const int kb = k0 + b * KB;
-    __syncthreads();
-    const bool more = b + 2 < n_stage;
+    wait_barrier(b + 2 < n_stage ? 1 : 0);  // stage b+2 (issued last) may stay in flight
+    const bool more = b + 3 < n_stage;
     const int pg = pg_next;
-    if (more) issue_k(pg, (b + 2) % NSTAGE);
-    pg_next = page_of_block(kb + 3 * KB);
+    if (more) issue_k(pg, (b + 3) % NSTAGE);
+    pg_next = page_of_block(kb + 4 * KB);
     step(mask_tag, true, s1, 0, s, 0, S_odd, S_even, kb + 32, Pa, Pb);
-    if (more) issue_v(pg, (b + 2) % NSTAGE);
+    if (more) issue_v(pg, (b + 3) % NSTAGE);
     step(mask_tag, true, s1, 1, s, 1, S_even, S_odd, kb + KB, Pb, Pa);
   };
   int b = 0;
@@ -635,7 +657,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   for (; b + 1 < n_stage; ++b) iteration(std::true_type{}, b);
   {
     const int s = b % NSTAGE;
-    __syncthreads();
+    wait_barrier(0);
     if (tail_partial) {                     // no wave has read this stage's V yet
       zero_tail(k0 + b * KB, s);
       __syncthreads();
