@@ -357,7 +357,9 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
     const int r = p / G, hh = p - r * G;
     const int m = it.row0 + (valid ? r : 0);
     const int row_tok = rows ? rows[m] : m;
-    pos_q[nb] = valid ? row_tok - seq0 : k1 - 1;
+    // Causal limit, clamped to the item's last key: the sub-blocks the
+    // pipeline runs past the item's end are then masked for every pair.
+    pos_q[nb] = valid ? min(row_tok - seq0, k1 - 1) : k1 - 1;
     wave_pmin = min(wave_pmin, pos_q[nb]);
     const uint16_t* qp = q + ((size_t)(q_index ? q_index[m] : m) * hq + g * G + hh) * 128 + hl * 8;
 #pragma unroll
@@ -478,7 +480,9 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) oacc[md][nb] = f32x16{};
   float m_run[2] = {-INFINITY, -INFINITY};   // running max, raw logit units
-  float l_run[2] = {0.f, 0.f};
+  // Running row sums as four partial sums per half (short add chains); the
+  // first add of each chain is an fma with alpha, which rescales them.
+  float lp[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   float alpha[2] = {1.f, 1.f};
   const float c = scale_log2;
 
@@ -503,11 +507,6 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
         oacc[md][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks * 4 + md], P[0][ks], oacc[md][0], 0, 0, 0);
         oacc[md][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks * 4 + md], P[1][ks], oacc[md][1], 0, 0, 0);
       }
-  };
-  auto pv = [&](int s, int h, const bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
-    bf16x8 vf[8];
-    load_v(s, h, vf);
-    pv_mfma(vf, P);
   };
 
   // Softmax of one query half of a sub-block (keys kb .. kb+31): S -> P (bf16,
@@ -534,21 +533,19 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
     alpha[nb] = __builtin_amdgcn_exp2f((m_run[nb] - m_new) * c);
     m_run[nb] = m_new;
     const float mc = m_new * c;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};      // four partial sums: short chains
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         p[i] = __builtin_amdgcn_exp2f(fmaf(S[ks * 8 + i], c, -mc));
-        ls[i & 3] += p[i];
+        lp[nb][i & 3] = (ks == 0 && i < 4) ? fmaf(lp[nb][i & 3], alpha[nb], p[i]) : lp[nb][i & 3] + p[i];
       }
       u32x4 pk;
 #pragma unroll
       for (int i = 0; i < 4; ++i) pk[i] = pack_bf2(p[2 * i], p[2 * i + 1]);
       P[ks] = __builtin_bit_cast(bf16x8, pk);
     }
-    l_run[nb] = l_run[nb] * alpha[nb] + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
     return any;
   };
   // O[:, nb] *= alpha[nb].  The empty volatile asm keeps this a real (rarely
@@ -578,21 +575,24 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   // can place the softmax VALU work between all 32 MFMAs of the step.  O is
   // rescaled at the end of the step (after PV j, before PV j+1) if the
   // softmax raised a running max.  MASK is compile-time.
-  auto step = [&](auto mask_tag, bool do_qk, int s_q, int h_q, int s_v, int h_v,
-                  f32x16 (&Sc)[2], f32x16 (&Sn)[2], int kb_soft, const bf16x8 (&P)[2][2],
-                  bf16x8 (&Pn)[2][2]) __attribute__((always_inline)) {
+  // Sub-block x lives in ring slot (x / 2) % NSTAGE, half x % 2.
+  auto step = [&](auto mask_tag, int j, f32x16 (&Sc)[2], f32x16 (&Sn)[2],
+                  const bf16x8 (&P)[2][2], bf16x8 (&Pn)[2][2]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     bf16x8 kf[8], vf[8];
-    if (do_qk) load_k(s_q, h_q, kf);
-    if (WITH_O) load_v(s_v, h_v, vf);
-    if (do_qk) {
-      qk_half(kf, 0, Sn[0]);
-      qk_half(kf, 1, Sn[1]);
-    }
+    load_k(((j + 2) >> 1) % NSTAGE, j & 1, kf);
+    if (WITH_O) load_v((j >> 1) % NSTAGE, j & 1, vf);
+    qk_half(kf, 0, Sn[0]);
+    qk_half(kf, 1, Sn[1]);
     if (WITH_O) pv_mfma(vf, P);
+    const int kb_soft = k0 + 32 * (j + 1);
     const bool r0 = softmax_half(Sc[0], MASK, kb_soft, 0, Pn[0]);
     const bool r1 = softmax_half(Sc[1], MASK, kb_soft, 1, Pn[1]);
+    // Pin the softmax results (P and the row sums) to this point so that
+    // their VALU work stays between this step's MFMAs.
     asm volatile("" : "+v"(Pn[0][0]), "+v"(Pn[0][1]), "+v"(Pn[1][0]), "+v"(Pn[1][1]));
+    asm volatile("" : "+v"(lp[0][0]), "+v"(lp[0][1]), "+v"(lp[0][2]), "+v"(lp[0][3]),
+                      "+v"(lp[1][0]), "+v"(lp[1][1]), "+v"(lp[1][2]), "+v"(lp[1][3]));
     if (WITH_O && r0) rescale_half(0);
     if (WITH_O && r1) rescale_half(1);
   };
@@ -600,21 +600,21 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   const int n_sub = (k1 - k0 + 31) / 32;
   const int n_stage = (n_sub + 1) / 2;
   const bool tail_partial = k0 + n_stage * KB - 1 > kmax;   // last stage holds keys past kmax
-  // Waits until at most `pending` of this wave's stage copies (the newest
-  // ones) are in flight, then the barrier.  pending is 0, 1 or 2 stages.
+  // Stage copies: stages 0-2 in the prologue, then one per iteration (stage
+  // b+3 at the start of iteration b, into the slot of stage b-1, which no
+  // wave reads after the barrier there).  Past the item's end the copies
+  // repeat its last page into slots no one reads any more, so the copy count
+  // per iteration is fixed and each wait is a constant: all but the newest
+  // stage's copies complete.
   constexpr int per_stage = WITH_O ? 8 : 4;   // copies per wave per stage
-  auto wait_barrier = [&](int pending_stages) __attribute__((always_inline)) {
-    if (pending_stages >= 2) vm_wait_barrier<2 * per_stage>();
-    else if (pending_stages == 1) vm_wait_barrier<per_stage>();
-    else vm_wait_barrier<0>();
-  };
-  // prologue: stages 0..2 in flight; S of sub-blocks 0 (even) and 1 (odd);
-  // softmax of sub-block 0
-  issue_stage(page_of_block(k0), 0);
-  if (n_stage > 1) issue_stage(page_of_block(k0 + KB), 1);
-  if (n_stage > 2) issue_stage(page_of_block(k0 + 2 * KB), 2);
-  int pg_next = page_of_block(k0 + 3 * KB);   // for stage 3
-  wait_barrier(min(n_stage, 3) - 1);         // stage 0 resident in every wave
+#pragma unroll
+  for (int i = 0; i < NSTAGE - 1; ++i) issue_stage(page_of_block(k0 + i * KB), i);
+  int pg_next = page_of_block(k0 + (NSTAGE - 1) * KB);
+  vm_wait_barrier<(NSTAGE - 2) * per_stage>();   // stage 0 resident
+  // (The last stage's tail is zeroed once the stage is resident; the next
+  // barrier orders those writes before any read of its values.)
+  if (tail_partial && n_stage == 1) zero_tail(k0, 0);
+  // prologue: S of sub-blocks 0 (even) and 1 (odd), softmax of sub-block 0
   f32x16 S_even[2], S_odd[2];
   bf16x8 Pa[2][2], Pb[2][2];
   {
@@ -630,45 +630,46 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
     if (softmax_half(S_even[1], mask0, k0, 1, Pa[1]) && WITH_O) rescale_half(1);
   }
 
-  // Iteration b: wait + barrier (stage b+1 resident, stage b-1 free), issue
-  // stage b+3 (K before step A, V before step B), then
-  //   step A: QK^T 2b+2 (stage b+1), PV 2b (stage b), softmax 2b+1;
-  //   step B: QK^T 2b+3 (stage b+1), PV 2b+1 (stage b), softmax 2b+2.
-  // Sub-blocks wholly below the tile's first query row need no causal
-  // mask: for b < b_plain both softmaxes are unmasked.  The last stage is
-  // peeled.
+  // Iteration b = steps 2b (A) and 2b+1 (B), after a barrier that makes
+  // stage b+1 resident and frees the slot of stage b-1:
+  //   step A: QK^T 2b+2 (stage b+1), PV 2b (stage b), softmax 2b+1
+  //   step B: QK^T 2b+3 (stage b+1), PV 2b+1 (stage b), softmax 2b+2
+  // The K half of stage b+3 is copied before step A, its V half before
+  // step B.  Work past the item's last sub-block is harmless (QK^T results
+  // unused, softmax fully masked since causal limits are clamped to the
+  // item's last key, reads inside the ring) except PV, so the loop exits
+  // right after the last PV.  Sub-blocks wholly below the tile's first query
+  // row need no causal mask: iterations b < b_plain are unmasked (and never
+  // reach the exit).
   const int tile_pmin = it.pad0;
-  const int n_plain_sub = max(0, (tile_pmin - k0 + 1) / 32);
-  const int b_plain = min(n_stage - 1, max(0, (n_plain_sub - 1) / 2));
-  auto iteration = [&](auto mask_tag, int b) __attribute__((always_inline)) {
-    const int s = b % NSTAGE, s1 = (b + 1) % NSTAGE;
-    const int kb = k0 + b * KB;
-    wait_barrier(b + 2 < n_stage ? 1 : 0);  // stage b+2 (issued last) may stay in flight
-    const bool more = b + 3 < n_stage;
-    const int pg = pg_next;
-    if (more) issue_k(pg, (b + 3) % NSTAGE);
-    pg_next = page_of_block(kb + 4 * KB);
-    step(mask_tag, true, s1, 0, s, 0, S_odd, S_even, kb + 32, Pa, Pb);
-    if (more) issue_v(pg, (b + 3) % NSTAGE);
-    step(mask_tag, true, s1, 1, s, 1, S_even, S_odd, kb + KB, Pb, Pa);
+  const int n_plain_sub = max(0, (min(tile_pmin, kmax) - k0 + 1) / 32);
+  const int b_plain = max(0, (n_plain_sub - 1) / 2);
+  auto barrier_copy_k = [&](int b) __attribute__((always_inline)) {
+    vm_wait_barrier<per_stage>();             // stage b+1 resident, b+2 may be in flight
+    if (tail_partial && b + 1 == n_stage - 1) zero_tail(k0 + (b + 1) * KB, (b + 1) % NSTAGE);
+    issue_k(pg_next, (b + 3) % NSTAGE);
+  };
+  auto copy_v = [&](int b) __attribute__((always_inline)) {
+    issue_v(pg_next, (b + 3) % NSTAGE);
+    pg_next = page_of_block(k0 + (b + NSTAGE) * KB);
   };
   int b = 0;
-  for (; b < b_plain; ++b) iteration(std::false_type{}, b);
-  for (; b + 1 < n_stage; ++b) iteration(std::true_type{}, b);
-  {
-    const int s = b % NSTAGE;
-    wait_barrier(0);
-    if (tail_partial) {                     // no wave has read this stage's V yet
-      zero_tail(k0 + b * KB, s);
-      __syncthreads();
-    }
-    if (2 * b + 1 < n_sub) {
-      step(std::true_type{}, false, s, 0, s, 0, S_odd, S_even, k0 + b * KB + 32, Pa, Pb);
-      if (WITH_O) pv(s, 1, Pb);
-    } else if (WITH_O) {
-      pv(s, 0, Pa);
-    }
+  for (; b < b_plain; ++b) {
+    barrier_copy_k(b);
+    step(std::false_type{}, 2 * b, S_odd, S_even, Pa, Pb);
+    copy_v(b);
+    step(std::false_type{}, 2 * b + 1, S_even, S_odd, Pb, Pa);
   }
+  for (;; ++b) {
+    barrier_copy_k(b);
+    step(std::true_type{}, 2 * b, S_odd, S_even, Pa, Pb);
+    if (2 * b + 1 >= n_sub) break;
+    copy_v(b);
+    step(std::true_type{}, 2 * b + 1, S_even, S_odd, Pb, Pa);
+    if (2 * b + 2 >= n_sub) break;
+  }
+  // No stage copy may still be writing LDS when the workgroup ends.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue ----------------------------------------------------------------
 #pragma unroll
@@ -678,7 +679,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
     const int r = p / G, hh = p - r * G;
     const int m = it.row0 + r;
     const int h = g * G + hh;
-    const float l_tot = half_sum(l_run[nb]);
+    const float l_tot = half_sum((lp[nb][0] + lp[nb][1]) + (lp[nb][2] + lp[nb][3]));
     const float m2 = m_run[nb] * c;                     // log2-domain max
     if (it.slot < 0) {
       if (lse && valid && hl == 0) lse[(size_t)m * hq + h] = (m2 + __log2f(l_tot)) * kLn2;
