@@ -31,8 +31,10 @@ CFLAGS = [
 ]
 SOURCES = ["api.cpp", "rope_realign.hip", "recompute_kv.hip", "attention.hip", "select.hip"]
 # Per-source extra flags.  The attention softmax never produces NaN (masked
-# logits are -inf), so max reductions need no NaN quieting.
-EXTRA = {"attention.hip": ["-fno-honor-nans"]}
+# logits are -inf), so max reductions need no NaN quieting.  Compiler-selected
+# MFMAs in attention write VGPRs (the score tiles the softmax reads); the
+# output accumulators are kept in AGPRs by the kernel's own asm.
+EXTRA = {"attention.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

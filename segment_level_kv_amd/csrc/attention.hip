@@ -41,7 +41,11 @@ namespace sx {
 namespace {
 
 constexpr int KB = 64;                 // keys per block
-constexpr int NSTAGE = 4;              // LDS ring depth (copies issued 2 stages ahead)
+constexpr int NSTAGE = 4;
+#ifndef SX_ATTN_HALVES
+#define SX_ATTN_HALVES 1
+#endif
+constexpr int kHalvesPerWave = SX_ATTN_HALVES;   // query halves of 32 pairs per wave (1 or 2)              // LDS ring depth (copies issued 2 stages ahead)
 constexpr int PAIRS = 256;             // (row, head) pairs per workgroup
 constexpr int kTargetItems = 768;      // work items aimed for (about 3 per CU)
 constexpr int kMinChunk = 1024;        // shortest key chunk of a split tile
@@ -321,8 +325,11 @@ __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
-template <bool WITH_O>
-__global__ __launch_bounds__(256, 1) void attn_fwd(
+// NB query halves (32 pairs each) per wave; 8 / NB waves share a tile of
+// 256 pairs.  NB = 1 puts two waves on each SIMD, so one wave's softmax and
+// LDS latency overlap the other's MFMAs.
+template <bool WITH_O, int NB>
+__global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_index,
     const int32_t* __restrict__ rows, sx_layout lay, int n_pages,
     const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool, int hkv, int G,
@@ -345,14 +352,16 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   const int k1 = min(it.k1, seq_len);
   if (k1 <= k0) return;
 
-  // ---- this lane's two pairs: query operand and positions -------------------
+  // ---- this lane's NB pairs: query operand and positions --------------------
+  constexpr int NW = 8 / NB;               // waves per workgroup
+  constexpr int NT = 64 * NW;              // threads per workgroup
   const int npairs = it.nrows * G;
-  int pos_q[2];
-  bf16x8 qf[2][8];
+  int pos_q[NB];
+  bf16x8 qf[NB][8];
   int wave_pmin = 0x7fffffff;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int p = 64 * w + 32 * nb + (lane & 31);
+  for (int nb = 0; nb < NB; ++nb) {
+    const int p = 32 * NB * w + 32 * nb + (lane & 31);
     const bool valid = p < npairs;
     const int r = p / G, hh = p - r * G;
     const int m = it.row0 + (valid ? r : 0);
@@ -376,8 +385,9 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
 
   // ---- K/V stages: global -> LDS directly (global_load_lds_dwordx4) ---------
   // A wave instruction writes 64 x 16 B = 1 KB of LDS, lane L at byte 16 L.
-  // Wave w copies page w of each 64-key block (its K and V page-heads, 4 KB
-  // each), so page ids are wave-uniform and per-lane offsets are constants.
+  // Each wave copies NB/2 of a page of each 64-key block (K rows 8*NB*w ..,
+  // and the matching head dimensions of its V page-head), 2*NB KB of K and
+  // of V, so page ids are wave-uniform and per-lane offsets are constants.
   // K stage: 64 key rows x 256 B; row R keeps 16-byte chunk c at slot
   //   c ^ (R & 15) (16 rows read together hit 16 distinct bank groups).
   // V stage: the page layout itself, [4 pages][128 d][16 keys]; row d keeps
@@ -389,12 +399,14 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   const int last_pi = min(kmax / kPage, lay.max_pages - 1);
   typedef __attribute__((address_space(1))) const void* gptr_t;
   typedef __attribute__((address_space(3))) void* lptr_t;
-  uint32_t koff[4], voff[4];               // byte offsets inside a page-head
+  constexpr int NCP = 2 * NB;              // copies of 1 KB per wave for K (and for V)
+  const int wpart = NB == 2 ? 0 : (w & 1);  // which half of its page a wave copies
+  uint32_t koff[NCP], voff[NCP];           // byte offsets inside a page-head
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int slot = 4 * i + (lane >> 4);
+  for (int i = 0; i < NCP; ++i) {
+    const int slot = 8 * wpart + 4 * i + (lane >> 4);            // key row inside the page
     koff[i] = (uint32_t)(slot * 128 + (((lane & 15) ^ slot) * 8)) * 2u;
-    const int d = 32 * i + (lane >> 1);
+    const int d = 64 * wpart + 32 * i + (lane >> 1);
     voff[i] = (uint32_t)(d * 16 + (((lane & 1) ^ ((d >> 3) & 1)) * 8)) * 2u;
   }
   const size_t head_bytes = (size_t)kPage * 128 * 2;      // one page-head, 4 KB
@@ -408,8 +420,9 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   const int wu = __builtin_amdgcn_readfirstlane(w);
   typedef __attribute__((address_space(4))) const int32_t* cptr_t;
   const cptr_t btc = (cptr_t)bt;
+  const int wpage = wu / (2 / NB);          // this wave's page of a block
   auto page_of_block = [&](int kb) __attribute__((always_inline)) {
-    const int pi = min(kb / kPage + wu, last_pi);
+    const int pi = min(kb / kPage + wpage, last_pi);
     const int pg = btc[pi];
     return (pg >= 0 && pg < n_pages) ? pg : 0;
   };
@@ -418,18 +431,19 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   auto issue_k = [&](int pg, int s) __attribute__((always_inline)) {
     const size_t base = ((size_t)pg * hkv + g) * head_bytes;
     const unsigned char* kp = reinterpret_cast<const unsigned char*>(kpool) + base;
-    unsigned char* kst = reinterpret_cast<unsigned char*>(&st[s].k[16 * wu][0]);
+    unsigned char* kst = reinterpret_cast<unsigned char*>(&st[s].k[8 * NB * wu][0]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NCP; ++i)
       __builtin_amdgcn_global_load_lds((gptr_t)(kp + koff[i]), (lptr_t)(kst + i * 1024), 16, 0, 0);
   };
   auto issue_v = [&](int pg, int s) __attribute__((always_inline)) {
     if (!WITH_O) return;
     const size_t base = ((size_t)pg * hkv + g) * head_bytes;
     const unsigned char* vp = reinterpret_cast<const unsigned char*>(vpool) + base;
-    unsigned char* vst = reinterpret_cast<unsigned char*>(&st[s].v[wu][0][0]);
+    unsigned char* vst =
+        reinterpret_cast<unsigned char*>(&st[s].v[wpage][NB == 2 ? 0 : 64 * (wu & 1)][0]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NCP; ++i)
       __builtin_amdgcn_global_load_lds((gptr_t)(vp + voff[i]), (lptr_t)(vst + i * 1024), 16, 0, 0);
   };
   auto issue_stage = [&](int pg, int s) __attribute__((always_inline)) {
@@ -442,7 +456,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
     const int first = kmax + 1 - kb;       // first key offset to clear
     if (!WITH_O || first >= KB) return;
     uint16_t* vs = &st[s].v[0][0][0];
-    for (int u = tid; u < 128 * KB; u += 256) {
+    for (int u = tid; u < 128 * KB; u += NT) {
       const int key = u & (KB - 1), d = u >> 6;
       if (key < first) continue;
       const int j = key >> 4, kk = key & 15;
@@ -474,16 +488,19 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
     for (int kk = 0; kk < 8; ++kk) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[nb][kk], S, 0, 0, 0);
   };
 
-  f32x16 oacc[4][2];
+  f32x16 oacc[4][NB];
 #pragma unroll
   for (int md = 0; md < 4; ++md)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) oacc[md][nb] = f32x16{};
-  float m_run[2] = {-INFINITY, -INFINITY};   // running max, raw logit units
+    for (int nb = 0; nb < NB; ++nb) oacc[md][nb] = f32x16{};
+  float m_run[NB], alpha[NB];                // running max (raw logit units), O scale
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) { m_run[nb] = -INFINITY; alpha[nb] = 1.f; }
   // Running row sums as four partial sums per half (short add chains); the
   // first add of each chain is an fma with alpha, which rescales them.
-  float lp[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  float alpha[2] = {1.f, 1.f};
+  float lp[NB][4];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) lp[nb][0] = lp[nb][1] = lp[nb][2] = lp[nb][3] = 0.f;
   const float c = scale_log2;
 
   // V^T operand of sub-block h of stage s: 8 x 16 B (all loaded before the
@@ -498,15 +515,24 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
         vf[ks * 4 + md] = *reinterpret_cast<const bf16x8*>(&st[s].v[2 * h + ks][d][half * 8]);
       }
   };
-  // O^T += V^T . P^T for one sub-block: 16 MFMAs.
-  auto pv_mfma = [&](const bf16x8 (&vf)[8], const bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
+  // O^T += V^T . P^T for one sub-block: 16 MFMAs.  Written as asm so that
+  // they accumulate in AGPRs while the QK^T MFMAs (compiler-selected, VGPR
+  // form) leave S in VGPRs for the softmax.  The compiler does not see these
+  // as MFMAs, so the code around them keeps the hazard distances itself:
+  // P is last written >= 2 instructions before (s_nop in the P pin), O is
+  // read only after >= 18 wait states (rescale and epilogue padding).
+#pragma unroll
+  for (int md = 0; md < 4; ++md)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(oacc[md][nb]));
+  auto pv_mfma = [&](const bf16x8 (&vf)[8], const bf16x8 (&P)[NB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int md = 0; md < 4; ++md) {
-        oacc[md][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks * 4 + md], P[0][ks], oacc[md][0], 0, 0, 0);
-        oacc[md][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks * 4 + md], P[1][ks], oacc[md][1], 0, 0, 0);
-      }
+      for (int md = 0; md < 4; ++md)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(oacc[md][nb]) : "v"(vf[ks * 4 + md]), "v"(P[nb][ks]));
   };
 
   // Softmax of one query half of a sub-block (keys kb .. kb+31): S -> P (bf16,
@@ -576,25 +602,29 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   // rescaled at the end of the step (after PV j, before PV j+1) if the
   // softmax raised a running max.  MASK is compile-time.
   // Sub-block x lives in ring slot (x / 2) % NSTAGE, half x % 2.
-  auto step = [&](auto mask_tag, int j, f32x16 (&Sc)[2], f32x16 (&Sn)[2],
-                  const bf16x8 (&P)[2][2], bf16x8 (&Pn)[2][2]) __attribute__((always_inline)) {
+  auto step = [&](auto mask_tag, int j, f32x16 (&Sc)[NB], f32x16 (&Sn)[NB],
+                  const bf16x8 (&P)[NB][2], bf16x8 (&Pn)[NB][2]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     bf16x8 kf[8], vf[8];
     load_k(((j + 2) >> 1) % NSTAGE, j & 1, kf);
     if (WITH_O) load_v((j >> 1) % NSTAGE, j & 1, vf);
-    qk_half(kf, 0, Sn[0]);
-    qk_half(kf, 1, Sn[1]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) qk_half(kf, nb, Sn[nb]);
     if (WITH_O) pv_mfma(vf, P);
     const int kb_soft = k0 + 32 * (j + 1);
-    const bool r0 = softmax_half(Sc[0], MASK, kb_soft, 0, Pn[0]);
-    const bool r1 = softmax_half(Sc[1], MASK, kb_soft, 1, Pn[1]);
-    // Pin the softmax results (P and the row sums) to this point so that
-    // their VALU work stays between this step's MFMAs.
-    asm volatile("" : "+v"(Pn[0][0]), "+v"(Pn[0][1]), "+v"(Pn[1][0]), "+v"(Pn[1][1]));
-    asm volatile("" : "+v"(lp[0][0]), "+v"(lp[0][1]), "+v"(lp[0][2]), "+v"(lp[0][3]),
-                      "+v"(lp[1][0]), "+v"(lp[1][1]), "+v"(lp[1][2]), "+v"(lp[1][3]));
-    if (WITH_O && r0) rescale_half(0);
-    if (WITH_O && r1) rescale_half(1);
+    bool r[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      r[nb] = softmax_half(Sc[nb], MASK, kb_soft, nb, Pn[nb]);
+      // Pin the softmax results (P and the row sums) to this point so that
+      // their VALU work stays between this step's MFMAs; the s_nop keeps
+      // the last P write two wait states ahead of the PV MFMAs that read it.
+      asm volatile("s_nop 1" : "+v"(Pn[nb][0]), "+v"(Pn[nb][1]));
+      asm volatile("" : "+v"(lp[nb][0]), "+v"(lp[nb][1]), "+v"(lp[nb][2]), "+v"(lp[nb][3]));
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      if (WITH_O && r[nb]) rescale_half(nb);
   };
 
   const int n_sub = (k1 - k0 + 31) / 32;
@@ -606,7 +636,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   // repeat its last page into slots no one reads any more, so the copy count
   // per iteration is fixed and each wait is a constant: all but the newest
   // stage's copies complete.
-  constexpr int per_stage = WITH_O ? 8 : 4;   // copies per wave per stage
+  constexpr int per_stage = WITH_O ? 2 * NCP : NCP;   // copies per wave per stage
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i) issue_stage(page_of_block(k0 + i * KB), i);
   int pg_next = page_of_block(k0 + (NSTAGE - 1) * KB);
@@ -615,19 +645,20 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
   // barrier orders those writes before any read of its values.)
   if (tail_partial && n_stage == 1) zero_tail(k0, 0);
   // prologue: S of sub-blocks 0 (even) and 1 (odd), softmax of sub-block 0
-  f32x16 S_even[2], S_odd[2];
-  bf16x8 Pa[2][2], Pb[2][2];
+  f32x16 S_even[NB], S_odd[NB];
+  bf16x8 Pa[NB][2], Pb[NB][2];
   {
     bf16x8 kf[8];
     load_k(0, 0, kf);
-    qk_half(kf, 0, S_even[0]);
-    qk_half(kf, 1, S_even[1]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) qk_half(kf, nb, S_even[nb]);
     load_k(0, 1, kf);
-    qk_half(kf, 0, S_odd[0]);
-    qk_half(kf, 1, S_odd[1]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) qk_half(kf, nb, S_odd[nb]);
     const bool mask0 = k0 + 31 > wave_pmin;
-    if (softmax_half(S_even[0], mask0, k0, 0, Pa[0]) && WITH_O) rescale_half(0);
-    if (softmax_half(S_even[1], mask0, k0, 1, Pa[1]) && WITH_O) rescale_half(1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      if (softmax_half(S_even[nb], mask0, k0, nb, Pa[nb]) && WITH_O) rescale_half(nb);
   }
 
   // Iteration b = steps 2b (A) and 2b+1 (B), after a barrier that makes
@@ -668,13 +699,14 @@ __global__ __launch_bounds__(256, 1) void attn_fwd(
     step(std::true_type{}, 2 * b + 1, S_even, S_odd, Pb, Pa);
     if (2 * b + 2 >= n_sub) break;
   }
-  // No stage copy may still be writing LDS when the workgroup ends.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // No stage copy may still be writing LDS when the workgroup ends; the
+  // last PV MFMAs finish before O is read.
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
 
   // ---- epilogue ----------------------------------------------------------------
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int p = 64 * w + 32 * nb + (lane & 31);
+  for (int nb = 0; nb < NB; ++nb) {
+    const int p = 32 * NB * w + 32 * nb + (lane & 31);
     const bool valid = p < npairs;
     const int r = p / G, hh = p - r * G;
     const int m = it.row0 + r;
@@ -846,10 +878,10 @@ sx_status launch_bf16(const sx_dims& dims, const sx_layout& lay, const void* q,
   sx_status st = check_launch("attention work list");
   if (st != SX_OK) return st;
   const size_t smem = NSTAGE * sizeof(Stage);
-  st = allow_lds((const void*)attn_fwd<WITH_O>, smem, "attention");
+  st = allow_lds((const void*)attn_fwd<WITH_O, kHalvesPerWave>, smem, "attention");
   if (st != SX_OK) return st;
   const float scale_log2 = kLog2e / sqrtf((float)dims.head_dim);
-  attn_fwd<WITH_O><<<L.max_items * hkv, 256, smem, stream>>>(
+  attn_fwd<WITH_O, kHalvesPerWave><<<L.max_items * hkv, 64 * (8 / kHalvesPerWave), smem, stream>>>(
       (const uint16_t*)q, q_index, rows, lay, kv.n_pages, (const uint16_t*)kv.k,
       (const uint16_t*)kv.v, hkv, G, (uint16_t*)o, lse, items, counters, part_ml, part_o,
       L.max_items, scale_log2);
