@@ -91,7 +91,7 @@ WsLayout ws_layout(int n_rows, int n_req, int G, int hkv, bool with_o) {
   w.merges = off;   off += align256((size_t)w.max_tiles * sizeof(MergeTile));
   w.part_ml = off;  off += align256((size_t)w.max_items * hkv * PAIRS * 2 * sizeof(float));
   w.part_o = off;
-  if (with_o) off += align256((size_t)w.max_items * hkv * PAIRS * 128 * sizeof(float));
+  if (with_o) off += align256((size_t)w.max_items * hkv * PAIRS * 128 * sizeof(uint16_t));
   w.total = off;
   return w;
 }
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
     const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool, int hkv, int G,
     uint16_t* __restrict__ o, float* __restrict__ lse, const AttnItem* __restrict__ items,
     const int32_t* __restrict__ counters, float* __restrict__ part_ml,
-    float* __restrict__ part_o, int max_slots, float scale_log2) {
+    uint16_t* __restrict__ part_o, int max_slots, float scale_log2) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Stage* st = reinterpret_cast<Stage*>(smem_raw);
 
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
   // they accumulate in AGPRs while the QK^T MFMAs (compiler-selected, VGPR
   // form) leave S in VGPRs for the softmax.  The compiler does not see these
   // as MFMAs, so the code around them keeps the hazard distances itself:
-  // P is last written >= 2 instructions before (s_nop in the P pin), O is
+  // P is last written >= 4 wait states before (s_nop in the P pin), O is
   // read only after >= 18 wait states (rescale and epilogue padding).
 #pragma unroll
   for (int md = 0; md < 4; ++md)
@@ -592,7 +592,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
         asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
                      : "+a"(oacc[md][nb][v]), "=&v"(t) : "v"(alpha[nb]));
       }
-    asm volatile("s_nop 4");
+    asm volatile("s_nop 7");
   };
 
   // One step j of a three-stage pipeline over 32-key sub-blocks: QK^T of
@@ -618,8 +618,8 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
       r[nb] = softmax_half(Sc[nb], MASK, kb_soft, nb, Pn[nb]);
       // Pin the softmax results (P and the row sums) to this point so that
       // their VALU work stays between this step's MFMAs; the s_nop keeps
-      // the last P write two wait states ahead of the PV MFMAs that read it.
-      asm volatile("s_nop 1" : "+v"(Pn[nb][0]), "+v"(Pn[nb][1]));
+      // the last P write four wait states ahead of the PV MFMAs that read it.
+      asm volatile("s_nop 3" : "+v"(Pn[nb][0]), "+v"(Pn[nb][1]));
       asm volatile("" : "+v"(lp[nb][0]), "+v"(lp[nb][1]), "+v"(lp[nb][2]), "+v"(lp[nb][3]));
     }
 #pragma unroll
@@ -734,17 +734,17 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
         part_ml[2 * pslot] = m2;
         part_ml[2 * pslot + 1] = l_tot;
       }
-      if (WITH_O) {                        // normalised partial output, fp32
+      if (WITH_O) {                        // normalised partial output, fp16
         const float inv = 1.f / l_tot;
-        float* op = part_o + pslot * 128 + 4 * hl;
+        uint16_t* op = part_o + pslot * 128 + 4 * hl;
 #pragma unroll
         for (int md = 0; md < 4; ++md)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            f32x4 v4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v4[e] = oacc[md][nb][4 * j + e] * inv;
-            *reinterpret_cast<f32x4*>(op + md * 32 + 8 * j) = v4;
+            u32x2 pk;
+            pk[0] = pack_h2(oacc[md][nb][4 * j] * inv, oacc[md][nb][4 * j + 1] * inv);
+            pk[1] = pack_h2(oacc[md][nb][4 * j + 2] * inv, oacc[md][nb][4 * j + 3] * inv);
+            *reinterpret_cast<u32x2*>(op + md * 32 + 8 * j) = pk;
           }
       }
     }
@@ -754,22 +754,26 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
 // Combines the key chunks of split tiles (chunk order fixed):
 //   M = max_c m_c,  w_c = l_c 2^(m_c - M),  O = sum_c w_c O_c / sum_c w_c,
 //   LSE = (M + log2 sum_c w_c) ln 2.
-// One workgroup per (merge tile, kv head); 16 threads per pair, 8 head
-// dimensions per thread.
+// One workgroup per (merge tile, kv head, group of 16 pairs); 16 threads per
+// pair, 8 head dimensions per thread.  Partial outputs are fp16 (normalised,
+// so bounded by the largest value magnitude).
+constexpr int kMergePairs = 16;
 template <bool WITH_O>
 __global__ __launch_bounds__(256) void attn_merge(
     const MergeTile* __restrict__ merges, const int32_t* __restrict__ counters, int hkv, int G,
-    const float* __restrict__ part_ml, const float* __restrict__ part_o,
+    const float* __restrict__ part_ml, const uint16_t* __restrict__ part_o,
     uint16_t* __restrict__ o, float* __restrict__ lse, int max_slots) {
-  const int g = blockIdx.x % hkv;
-  const int mi = blockIdx.x / hkv;
+  const int grp = blockIdx.x % (PAIRS / kMergePairs);
+  const int g = (blockIdx.x / (PAIRS / kMergePairs)) % hkv;
+  const int mi = blockIdx.x / (PAIRS / kMergePairs) / hkv;
   if (mi >= counters[1]) return;
   const MergeTile mt = merges[mi];
   if (mt.slot0 < 0 || mt.slot0 + mt.n_chunks > max_slots) return;
   const int hq = G * hkv;
   const int npairs = mt.nrows * G;
   const int sub = threadIdx.x & 15;
-  for (int p = threadIdx.x >> 4; p < npairs; p += 16) {
+  const int p = grp * kMergePairs + (threadIdx.x >> 4);
+  if (p < npairs) {
     float M = -INFINITY;
     for (int c = 0; c < mt.n_chunks; ++c) {
       const size_t ps = ((size_t)(mt.slot0 + c) * hkv + g) * PAIRS + p;
@@ -782,12 +786,12 @@ __global__ __launch_bounds__(256) void attn_merge(
       const float wc = part_ml[2 * ps + 1] * __builtin_amdgcn_exp2f(part_ml[2 * ps] - M);
       wsum += wc;
       if (WITH_O) {
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(part_o + ps * 128 + sub * 8);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(part_o + ps * 128 + sub * 8 + 4);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(part_o + ps * 128 + sub * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[e] = fmaf(wc, a0[e], acc[e]);
-          acc[4 + e] = fmaf(wc, a1[e], acc[4 + e]);
+          const f32x2_t a = unpack_h2(raw[e]);
+          acc[2 * e] = fmaf(wc, a[0], acc[2 * e]);
+          acc[2 * e + 1] = fmaf(wc, a[1], acc[2 * e + 1]);
         }
       }
     }
@@ -869,7 +873,7 @@ sx_status launch_bf16(const sx_dims& dims, const sx_layout& lay, const void* q,
   AttnItem* items = reinterpret_cast<AttnItem*>(base + L.items);
   MergeTile* merges = reinterpret_cast<MergeTile*>(base + L.merges);
   float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
-  float* part_o = WITH_O ? reinterpret_cast<float*>(base + L.part_o) : nullptr;
+  uint16_t* part_o = WITH_O ? reinterpret_cast<uint16_t*>(base + L.part_o) : nullptr;
   const int M = rows_per_tile(G);
   const int target = items_per_head(hkv);
   build_work<<<1, kBuildThreads, (size_t)(lay.n_req + 1) * sizeof(int), stream>>>(row_start, rows, lay.seq_start, lay.n_req, n_rows, M,
@@ -887,7 +891,7 @@ sx_status launch_bf16(const sx_dims& dims, const sx_layout& lay, const void* q,
       L.max_items, scale_log2);
   st = check_launch("attention");
   if (st != SX_OK) return st;
-  attn_merge<WITH_O><<<L.max_tiles * hkv, 256, 0, stream>>>(merges, counters, hkv, G, part_ml,
+  attn_merge<WITH_O><<<L.max_tiles * hkv * (PAIRS / kMergePairs), 256, 0, stream>>>(merges, counters, hkv, G, part_ml,
                                                            part_o, (uint16_t*)o, lse, L.max_items);
   return check_launch("attention merge");
 }

@@ -5,10 +5,9 @@
 //   [q | k | v] = x[rows] . W_qkv^T ;  q, k rotated by R_pos ;
 //   k, v scattered into the request's pages, q written densely.
 //
-// bf16 path: MFMA GEMM (v_mfma_f32_32x32x16_bf16), 128x128 output tiles
+// bf16 path: MFMA GEMM (v_mfma_f32_32x32x16_bf16), 256x128 output tiles
 // (one tile column = one head of 128, so both halves of every rotate-half
-// pair are in the tile), K-step 64 staged through LDS with a double buffer
-// and register prefetch.  Tiles are assigned XCD-contiguously (workgroup b
+// pair are in the tile).  Tiles are assigned XCD-contiguously (workgroup b
 // runs on XCD b % 8) and grouped 4 row-tiles at a time so that concurrently
 // running workgroups share W and X slices in their XCD's L2.  The epilogue
 // stages the fp32 tile in LDS, applies RoPE with the fp64-built table,
@@ -20,30 +19,38 @@ namespace sx {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDK = BK + 8;          // padded LDS row (elements) against bank conflicts
-constexpr int LDC = BN + 4;
+constexpr int BN = 128, BK = 64;
+constexpr int LDC = BN + 4;          // padded fp32 row of the staged output tile
 constexpr int GROUP_M = 4;
 
-struct GemmSmem {
+// bf16 GEMM, 256 x 128 output tiles (256 rows, one head).  K-steps of 64
+// go global -> LDS directly (global_load_lds_dwordx4) into a ring of three
+// stages; each 128-byte LDS row keeps its 16-byte chunk c at position
+// c ^ (row & 7), so the 32 rows an MFMA operand read touches spread over
+// all banks.  Four waves, each 128 rows x 64 columns = 4 x 2 MFMA tiles of
+// 32 x 32 (acc in AGPRs); the operands of k-slice ks+1 are read from LDS
+// while the MFMAs of slice ks run.
+constexpr int BM2 = 256, NST2 = 3;
+struct Gemm2Stage {
+  uint16_t a[BM2][BK];
+  uint16_t b[BN][BK];
+};
+struct Gemm2Smem {
   union {
-    struct {
-      uint16_t a[2][BM][LDK];
-      uint16_t b[2][BN][LDK];
-    } ab;
-    float c[BM][LDC];
+    Gemm2Stage st[NST2];
+    float c[BM2][LDC];
   };
-  int32_t row_req[BM];
-  int32_t row_idx[BM];
+  int32_t row_req[BM2];
+  int32_t row_idx[BM2];
 };
 
-__global__ __launch_bounds__(256) void qkv_gemm_bf16(
+__global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
     const uint16_t* __restrict__ x, int hidden, const int32_t* __restrict__ rows, int n_rows,
     const uint16_t* __restrict__ w, int head0, int n_tiles_m, int n_tiles_n, sx_layout lay,
     int n_pages, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
     uint16_t* __restrict__ q_out, int hq, int hkv) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  GemmSmem& sm = *reinterpret_cast<GemmSmem*>(smem_raw);
+  Gemm2Smem& sm = *reinterpret_cast<Gemm2Smem*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -58,12 +65,11 @@ __global__ __launch_bounds__(256) void qkv_gemm_bf16(
   const int within = t % (GROUP_M * n_tiles_n);
   const int mt = first_m + within % gsz;
   const int nt = within / gsz;
-  const int m0 = mt * BM;
+  const int m0 = mt * BM2;
   const int head = head0 + nt;                 // 0..hq-1: Q, then K heads, then V heads
   const uint16_t* wt = w + (size_t)head * 128 * hidden;
 
-  // ---- per-row request / index ---------------------------------------------
-  if (tid < BM) {
+  {
     int r = -1, idx = 0;
     if (m0 + tid < n_rows) {
       const int tok = rows[m0 + tid];
@@ -74,78 +80,102 @@ __global__ __launch_bounds__(256) void qkv_gemm_bf16(
     sm.row_idx[tid] = idx;
   }
 
-  // ---- global -> register loaders (4 x 16 B per thread for A and for B) ---
-  const uint16_t* a_src[4];
-  const uint16_t* b_src[4];
-  int l_row[4], l_chunk[4];
+  // ---- copy plan: lane L of copy i moves one 16-byte chunk --------------
+  // A: rows 64*wave + 8*i + L/8 (i < 8); B: rows 32*wave + 8*i + L/8 (i < 4).
+  // Row R's chunk c is stored at chunk position c ^ (R & 7) = L % 8, so the
+  // lane loads chunk (L % 8) ^ (R & 7).  Rows past n_rows (or with a token
+  // outside the sequence) read row 0 of x: finite data whose results are
+  // never stored.
+  typedef __attribute__((address_space(1))) const void* gptr_t;
+  typedef __attribute__((address_space(3))) void* lptr_t;
+  size_t a_off[8];                           // byte offsets of this lane's chunks at k = 0
+  uint32_t b_off[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int R = 64 * wave + 8 * i + (lane >> 3);
+    const int m = m0 + R;
+    int tok = m < n_rows ? rows[m] : 0;
+    if (tok < 0 || tok >= lay.n_tok) tok = 0;
+    a_off[i] = ((size_t)tok * hidden + (size_t)(((lane & 7) ^ (R & 7)) * 8)) * 2u;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int u = tid + 256 * i;
-    l_row[i] = u >> 3;
-    l_chunk[i] = u & 7;
-    const int m = m0 + l_row[i];
-    int tok = (m < n_rows) ? rows[m] : -1;
-    if (tok < 0 || tok >= lay.n_tok) tok = -1;
-    a_src[i] = tok >= 0 ? x + (size_t)tok * hidden + l_chunk[i] * 8 : nullptr;
-    b_src[i] = wt + (size_t)l_row[i] * hidden + l_chunk[i] * 8;
+    const int R = 32 * wave + 8 * i + (lane >> 3);
+    b_off[i] = ((uint32_t)R * (uint32_t)hidden + (uint32_t)(((lane & 7) ^ (R & 7)) * 8)) * 2u;
   }
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int k0) {
+  const unsigned char* xb = reinterpret_cast<const unsigned char*>(x);
+  const unsigned char* wb = reinterpret_cast<const unsigned char*>(wt);
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  const int n_k = hidden / BK;
+  // Stage kt (k = 64 kt, clamped to the last step: the copies past the end
+  // repeat it into a ring slot no one reads any more, keeping 12 copies per
+  // stage so each wait is a constant).
+  auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
+    const uint32_t kb = (uint32_t)min(kt, n_k - 1) * BK * 2u;
+    unsigned char* as = reinterpret_cast<unsigned char*>(&sm.st[slot].a[64 * wu][0]);
+    unsigned char* bs = reinterpret_cast<unsigned char*>(&sm.st[slot].b[32 * wu][0]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = a_src[i] ? *reinterpret_cast<const u32x4*>(a_src[i] + k0) : u32x4{0, 0, 0, 0};
-      rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + k0);
-    }
-  };
-  auto lstore = [&](int buf) {
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(xb + a_off[i] + kb), (lptr_t)(as + i * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&sm.ab.a[buf][l_row[i]][l_chunk[i] * 8]) = ra[i];
-      *reinterpret_cast<u32x4*>(&sm.ab.b[buf][l_row[i]][l_chunk[i] * 8]) = rb[i];
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(wb + b_off[i] + kb), (lptr_t)(bs + i * 1024), 16, 0, 0);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  const int n_k = hidden / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  const int lr = lane & 31, lh = lane >> 5;
+  issue(0, 0);
+  issue(1, 1);
   for (int kt = 0; kt < n_k; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_k) gload((kt + 1) * BK);
+    const int slot = kt % NST2;
+    // stage kt resident in every wave (stage kt+1's 12 copies may be in
+    // flight); the slot of stage kt-1 is free for stage kt+2
+    asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    issue(kt + 2, (kt + 2) % NST2);
+    const Gemm2Stage& S = sm.st[slot];
+    // Operands of k-slice ks+1 are read while the MFMAs of slice ks run.
+    bf16x8 af[2][4], bfr[2][2];
+    auto load = [&](int ks, int buf) __attribute__((always_inline)) {
+      const int ch = 2 * ks + lh;              // 16-byte chunk of this lane's k range
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int R = wm * 128 + i * 32 + lr;
+        af[buf][i] = *reinterpret_cast<const bf16x8*>(&S.a[R][(ch ^ (R & 7)) * 8]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int R = wn * 64 + j * 32 + lr;
+        bfr[buf][j] = *reinterpret_cast<const bf16x8*>(&S.b[R][(ch ^ (R & 7)) * 8]);
+      }
+    };
+    load(0, 0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[2], bfr[2];
+      if (ks + 1 < BK / 16) load(ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);     // keep those reads ahead of this slice's MFMAs
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(&sm.ab.a[buf][wm * 64 + i * 32 + lr][ks * 16 + lk]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&sm.ab.b[buf][wn * 64 + j * 32 + lr][ks * 16 + lk]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < n_k) lstore(buf ^ 1);
-    __syncthreads();
   }
+  // all copies landed and every wave done with the ring before it becomes C
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // ---- epilogue: fp32 tile -> LDS ------------------------------------------
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int r = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         const int c = wn * 64 + j * 32 + (lane & 31);
         sm.c[r][c] = acc[i][j][v];
       }
@@ -155,9 +185,7 @@ __global__ __launch_bounds__(256) void qkv_gemm_bf16(
     // Q or K head: rotate-half pairs (e, e+64), 8 pairs per unit.
     const bool is_q = head < hq;
     const int g = head - hq;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = tid + 256 * i;
+    for (int u = tid; u < BM2 * 8; u += 256) {
       const int m = u >> 3, c = u & 7;
       const int r = sm.row_req[m];
       if (r < 0) continue;
@@ -192,8 +220,8 @@ __global__ __launch_bounds__(256) void qkv_gemm_bf16(
   } else {
     // V head: page layout [d][slot]; consecutive lanes take consecutive rows.
     const int g = head - hq - hkv;
-    for (int u = tid; u < BM * 128; u += 256) {
-      const int m = u & (BM - 1), e = u >> 7;
+    for (int u = tid; u < BM2 * 128; u += 256) {
+      const int m = u & (BM2 - 1), e = u >> 8;
       const int r = sm.row_req[m];
       if (r < 0) continue;
       const int idx = sm.row_idx[m];
@@ -265,13 +293,13 @@ sx_status launch_recompute(const sx_dims& dims, const sx_layout& lay, const void
   const int head0 = q_out ? 0 : hq;
   const int n_heads = hq + 2 * hkv - head0;
   if (dims.dtype == SX_BF16) {
-    const int mt = (n_rows + BM - 1) / BM;
+    const int mt = (n_rows + BM2 - 1) / BM2;
     const int total = mt * n_heads;
     const int grid = ((total + 7) / 8) * 8;
-    const size_t smem = sizeof(GemmSmem);
-    const sx_status st = allow_lds((const void*)qkv_gemm_bf16, smem, "sx_recompute_kv");
+    const size_t smem = sizeof(Gemm2Smem);
+    const sx_status st = allow_lds((const void*)qkv_gemm256_bf16, smem, "sx_recompute_kv");
     if (st != SX_OK) return st;
-    qkv_gemm_bf16<<<grid, 256, smem, stream>>>(
+    qkv_gemm256_bf16<<<grid, 256, smem, stream>>>(
         (const uint16_t*)x, dims.hidden, rows, n_rows, (const uint16_t*)w_qkv, head0, mt, n_heads,
         lay, kv.n_pages, (uint16_t*)kv.k, (uint16_t*)kv.v, (uint16_t*)q_out, hq, hkv);
   } else {

@@ -37,6 +37,16 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Two fp32 values -> packed fp16 pair (round to nearest even), and back.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
+}
+__device__ __forceinline__ f32x2_t unpack_h2(uint32_t v) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2_t, v), f32x2_t);
+}
+
 // Request owning packed token `tok` (seq_start ascending, n_req+1 entries).
 // Returns -1 if tok is outside [seq_start[0], seq_start[n_req]).
 __device__ __forceinline__ int find_request(const int32_t* __restrict__ seq_start, int n_req, int tok) {
