@@ -597,20 +597,25 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
 
   // One step j of a three-stage pipeline over 32-key sub-blocks: QK^T of
   // sub-block j+2 (into Sn), PV of sub-block j (with P), softmax of
-  // sub-block j+1 (Sc -> Pn).  The three are independent, so the scheduler
-  // can place the softmax VALU work between all 32 MFMAs of the step.  O is
-  // rescaled at the end of the step (after PV j, before PV j+1) if the
-  // softmax raised a running max.  MASK is compile-time.
+  // sub-block j+1 (Sc -> Pn).  The three are independent; the MFMAs run as
+  // one phase and the softmax as another, in the order SOFT_FIRST gives (a
+  // scheduling barrier keeps the phases apart).  O is rescaled at the end
+  // of the step (after PV j, before PV j+1) if the softmax raised a running
+  // max.  MASK and SOFT_FIRST are compile-time.
   // Sub-block x lives in ring slot (x / 2) % NSTAGE, half x % 2.
   auto step = [&](auto mask_tag, int j, f32x16 (&Sc)[NB], f32x16 (&Sn)[NB],
-                  const bf16x8 (&P)[NB][2], bf16x8 (&Pn)[NB][2]) __attribute__((always_inline)) {
+                  const bf16x8 (&P)[NB][2], bf16x8 (&Pn)[NB][2], auto order_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool SOFT_FIRST = decltype(order_tag)::value;
     bf16x8 kf[8], vf[8];
     load_k(((j + 2) >> 1) % NSTAGE, j & 1, kf);
     if (WITH_O) load_v((j >> 1) % NSTAGE, j & 1, vf);
+    if (!SOFT_FIRST) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) qk_half(kf, nb, Sn[nb]);
-    if (WITH_O) pv_mfma(vf, P);
+      for (int nb = 0; nb < NB; ++nb) qk_half(kf, nb, Sn[nb]);
+      if (WITH_O) pv_mfma(vf, P);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const int kb_soft = k0 + 32 * (j + 1);
     bool r[NB];
 #pragma unroll
@@ -621,6 +626,12 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
       // the last P write four wait states ahead of the PV MFMAs that read it.
       asm volatile("s_nop 3" : "+v"(Pn[nb][0]), "+v"(Pn[nb][1]));
       asm volatile("" : "+v"(lp[nb][0]), "+v"(lp[nb][1]), "+v"(lp[nb][2]), "+v"(lp[nb][3]));
+    }
+    if (SOFT_FIRST) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) qk_half(kf, nb, Sn[nb]);
+      if (WITH_O) pv_mfma(vf, P);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -684,21 +695,27 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
     issue_v(pg_next, (b + 3) % NSTAGE);
     pg_next = page_of_block(k0 + (b + NSTAGE) * KB);
   };
-  int b = 0;
-  for (; b < b_plain; ++b) {
-    barrier_copy_k(b);
-    step(std::false_type{}, 2 * b, S_odd, S_even, Pa, Pb);
-    copy_v(b);
-    step(std::false_type{}, 2 * b + 1, S_even, S_odd, Pb, Pa);
-  }
-  for (;; ++b) {
-    barrier_copy_k(b);
-    step(std::true_type{}, 2 * b, S_odd, S_even, Pa, Pb);
-    if (2 * b + 1 >= n_sub) break;
-    copy_v(b);
-    step(std::true_type{}, 2 * b + 1, S_even, S_odd, Pb, Pa);
-    if (2 * b + 2 >= n_sub) break;
-  }
+  auto run = [&](auto order) __attribute__((always_inline)) {
+    int b = 0;
+    for (; b < b_plain; ++b) {
+      barrier_copy_k(b);
+      step(std::false_type{}, 2 * b, S_odd, S_even, Pa, Pb, order);
+      copy_v(b);
+      step(std::false_type{}, 2 * b + 1, S_even, S_odd, Pb, Pa, order);
+    }
+    for (;; ++b) {
+      barrier_copy_k(b);
+      step(std::true_type{}, 2 * b, S_odd, S_even, Pa, Pb, order);
+      if (2 * b + 1 >= n_sub) break;
+      copy_v(b);
+      step(std::true_type{}, 2 * b + 1, S_even, S_odd, Pb, Pa, order);
+      if (2 * b + 2 >= n_sub) break;
+    }
+  };
+  // The two waves of a SIMD (w and w + 4) run each step's MFMAs and its
+  // softmax in opposite orders, so that one's VALU work tends to meet the
+  // other's MFMAs; each order is a separate copy of the loop.
+  if (NB == 1 && wu >= 4) run(std::true_type{}); else run(std::false_type{});
   // No stage copy may still be writing LDS when the workgroup ends; the
   // last PV MFMAs finish before O is read.
   asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
