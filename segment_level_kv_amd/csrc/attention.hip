@@ -51,6 +51,7 @@ constexpr int kTargetItems = 768;      // work items aimed for (about 3 per CU)
 constexpr int kMinChunk = 1024;        // shortest key chunk of a split tile
 constexpr int kBuildThreads = 1024;
 constexpr int kSortBuckets = 2048;     // item length buckets (64 keys each)
+constexpr int kFullKeys = 1024;        // sort keys for full chunks (by chunk index)
 
 struct Stage {
   uint16_t k[KB][128];        // 64 key rows, 16-byte chunks XOR-swizzled by row
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_work(
     AttnItem* __restrict__ items, MergeTile* __restrict__ merges, int32_t* __restrict__ counters) {
   extern __shared__ int roff[];              // first tile of each request
   __shared__ int sh_scan[kBuildThreads / 64];
-  __shared__ int hist[kSortBuckets];
+  __shared__ int hist[kFullKeys + kSortBuckets];
   __shared__ long long s_work[kBuildThreads / 64];
   const int tid = threadIdx.x;
 
@@ -225,12 +226,16 @@ __global__ __launch_bounds__(kBuildThreads) void build_work(
   }
   const int n_items = min(item_base, max_items);
 
-  // ---- items, counting-sorted by length (longest first) ----------------------------
-  for (int i = tid; i < kSortBuckets; i += kBuildThreads) hist[i] = 0;
+  // ---- items, counting-sorted ------------------------------------------------------
+  // Chunks of a split tile sit on a grid shared by all tiles: full chunks
+  // [c*chunk, (c+1)*chunk) below the block holding pmin, then the remainder
+  // up to that block, then the last chunk from that block to pmax (so every
+  // row sees at least one key of every chunk).  Order: full chunks first,
+  // by chunk index (the workgroups running together on an XCD then stream
+  // the same keys of one kv head, which its L2 shares), then the other items
+  // longest first.
+  for (int i = tid; i < kFullKeys + kSortBuckets; i += kBuildThreads) hist[i] = 0;
   __syncthreads();
-  // chunk c of tile t: the last chunk starts at the block holding pmin so that
-  // every row sees at least one key of every chunk; earlier chunks step back
-  // by `chunk` keys (the first one may be shorter).
   auto chunk_range = [&](const TileInfo& T, int c, int& k0, int& k1) {
     if (T.n_chunks == 1) {
       k0 = 0;
@@ -238,28 +243,31 @@ __global__ __launch_bounds__(kBuildThreads) void build_work(
       return;
     }
     const int last_start = (T.pmin / KB) * KB;
-    const int back = T.n_chunks - 1 - c;       // chunks after this one
-    if (back == 0) {
+    if (c == T.n_chunks - 1) {
       k0 = last_start;
       k1 = T.pmax + 1;
     } else {
-      k1 = last_start - (back - 1) * chunk;
-      k0 = max(0, k1 - chunk);
+      k0 = c * chunk;
+      k1 = min(k0 + chunk, last_start);
     }
+  };
+  auto sort_key = [&](const TileInfo& T, int c, int k0, int k1) {
+    if (T.n_chunks > 1 && c < T.n_chunks - 1 && k1 - k0 == chunk) return min(c, kFullKeys - 1);
+    return kFullKeys + kSortBuckets - 1 - min((k1 - k0 - 1) / KB, kSortBuckets - 1);
   };
   for (int t = tid; t < n_tiles; t += kBuildThreads) {
     const TileInfo T = tiles[t];
     for (int c = 0; c < T.n_chunks; ++c) {
       int k0, k1;
       chunk_range(T, c, k0, k1);
-      const int bkt = min((k1 - k0 - 1) / KB, kSortBuckets - 1);
-      atomicAdd(&hist[kSortBuckets - 1 - bkt], 1);
+      atomicAdd(&hist[sort_key(T, c, k0, k1)], 1);
     }
   }
   __syncthreads();
-  // exclusive scan of the histogram (longest bucket first)
+  // exclusive scan of the histogram
   {
-    constexpr int PER = kSortBuckets / kBuildThreads;
+    constexpr int PER = (kFullKeys + kSortBuckets) / kBuildThreads;
+    static_assert(PER * kBuildThreads == kFullKeys + kSortBuckets, "histogram split");
     int loc[PER], s = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -280,8 +288,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_work(
     for (int c = 0; c < T.n_chunks; ++c) {
       int k0, k1;
       chunk_range(T, c, k0, k1);
-      const int bkt = min((k1 - k0 - 1) / KB, kSortBuckets - 1);
-      const int pos = atomicAdd(&hist[kSortBuckets - 1 - bkt], 1);
+      const int pos = atomicAdd(&hist[sort_key(T, c, k0, k1)], 1);
       if (pos >= max_items) continue;
       AttnItem it;
       it.req = T.req;
