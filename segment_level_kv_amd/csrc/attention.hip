@@ -47,7 +47,7 @@ constexpr int NSTAGE = 4;
 #endif
 constexpr int kHalvesPerWave = SX_ATTN_HALVES;   // query halves of 32 pairs per wave (1 or 2)              // LDS ring depth (copies issued 2 stages ahead)
 constexpr int PAIRS = 256;             // (row, head) pairs per workgroup
-constexpr int kTargetItems = 768;      // work items aimed for (about 3 per CU)
+constexpr int kTargetItems = 256;      // work items aimed for (one per CU); tiles are split only below it
 constexpr int kMinChunk = 1024;        // shortest key chunk of a split tile
 constexpr int kBuildThreads = 1024;
 constexpr int kSortBuckets = 2048;     // item length buckets (64 keys each)
