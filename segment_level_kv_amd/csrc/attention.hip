@@ -365,6 +365,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
   const int npairs = it.nrows * G;
   int pos_q[NB];
   bf16x8 qf[NB][8];
+  const uint16_t* qptr[NB];
   int wave_pmin = 0x7fffffff;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -377,15 +378,9 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
     // pipeline runs past the item's end are then masked for every pair.
     pos_q[nb] = valid ? min(row_tok - seq0, k1 - 1) : k1 - 1;
     wave_pmin = min(wave_pmin, pos_q[nb]);
-    const uint16_t* qp = q + ((size_t)(q_index ? q_index[m] : m) * hq + g * G + hh) * 128 + hl * 8;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      u32x4 raw = valid ? *reinterpret_cast<const u32x4*>(qp + kk * 16) : u32x4{0, 0, 0, 0};
-      qf[nb][kk] = __builtin_bit_cast(bf16x8, raw);
-      // Q stays in AGPRs for the whole kernel (MFMA reads its B operand from
-      // there), leaving the VGPRs to the softmax and the LDS operands.
-      asm volatile("" : "+a"(qf[nb][kk]));
-    }
+    // (A pair past the tile reads a valid row's Q; its results are never
+    // stored.)
+    qptr[nb] = q + ((size_t)(q_index ? q_index[m] : m) * hq + g * G + hh) * 128 + hl * 8;
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wave_pmin = min(wave_pmin, __shfl_xor(wave_pmin, off));
@@ -658,6 +653,18 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i) issue_stage(page_of_block(k0 + i * KB), i);
   int pg_next = page_of_block(k0 + (NSTAGE - 1) * KB);
+  // Q is loaded after the first stage copies are on their way (one wait
+  // covers both) and stays in AGPRs for the whole kernel (MFMA reads its B
+  // operand from there), leaving the VGPRs to the softmax and LDS operands.
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qf[nb][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qptr[nb] + kk * 16));
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+a"(qf[nb][kk]));
   vm_wait_barrier<(NSTAGE - 2) * per_stage>();   // stage 0 resident
   // (The last stage's tail is zeroed once the stage is resident; the next
   // barrier orders those writes before any read of its values.)
