@@ -140,8 +140,9 @@ def realign_segment(k_cached, v_cached, p_src: int, p_dst: int, theta: float, dt
 FALLBACK_TOKENS = 64
 
 
-def plan_request(pieces, ratio, fallback_tokens: int = FALLBACK_TOKENS) -> dict:
-    """Token classes and the selection budget of one request (§3.2).
+def plan_request(pieces, ratio, fallback_tokens: int = FALLBACK_TOKENS,
+                 overflow_tokens: int = 0) -> dict:
+    """Token classes and the selection budget of one request (§3.2, §3.3).
 
     pieces: ordered list of ("reuse", L) or ("new", L) runs; positions are
     0-based token indices in the request (T = sum of L).  Empty runs are
@@ -157,8 +158,19 @@ def plan_request(pieces, ratio, fallback_tokens: int = FALLBACK_TOKENS) -> dict:
     ratio is read as a fraction of the reused tokens, so that ratio 100%
     recomputes every token).
 
+    Overflow (§3.3, second paragraph), off when overflow_tokens is 0.
+    Reading taken: a block is overflow_tokens tokens (the 16-token KV page
+    of a block-aligned layout); for every maximal run of non-reused pieces,
+    the last min(overflow_tokens, L) tokens of the reused piece right before
+    it and the first min(overflow_tokens, L) tokens of the reused piece right
+    after it join the Sparse-Q set, as the fallback tokens do: the paragraph
+    widens the Sparse-Q index interval itself, so the widened rows get
+    queries, fresh K/V, probe and attend.  They are thereby no selection
+    candidates and the budget k counts only the remaining reused tokens.
+
     Returns dict(T, is_reuse[bool T], sq[int, ascending], cand[int,
-    ascending], k, fallback[bool]).
+    ascending], k, fallback[bool], overflow[int, ascending]: the tokens the
+    overflow step marked, whether or not the fallback also took them).
     """
     pieces = [(kind, int(n)) for kind, n in pieces if int(n) > 0]
     for kind, _ in pieces:
@@ -180,13 +192,29 @@ def plan_request(pieces, ratio, fallback_tokens: int = FALLBACK_TOKENS) -> dict:
         m = min(fallback_tokens, n_last)
         in_sq[T - m:T] = True
         fallback = True
+    if overflow_tokens < 0:
+        raise ValueError("overflow_tokens must be >= 0")
+    widened = np.zeros(T, dtype=bool)
+    if overflow_tokens > 0:
+        starts = np.cumsum([0] + [n for _, n in pieces])
+        for p, (kind, n) in enumerate(pieces):
+            if kind != "new":
+                continue
+            if p > 0 and pieces[p - 1][0] == "reuse":          # previous reuse segment
+                m = min(overflow_tokens, pieces[p - 1][1])
+                widened[starts[p] - m:starts[p]] = True
+            if p + 1 < len(pieces) and pieces[p + 1][0] == "reuse":   # next reuse segment
+                m = min(overflow_tokens, pieces[p + 1][1])
+                widened[starts[p + 1]:starts[p + 1] + m] = True
+        in_sq |= widened
     sq = np.flatnonzero(in_sq)
     cand = np.flatnonzero(is_reuse & ~in_sq)
     num, den = int(ratio[0]), int(ratio[1])
     if den <= 0 or num < 0 or num > den:
         raise ValueError("ratio must be a fraction in [0, 1]")
     k = (num * len(cand)) // den
-    return dict(T=T, is_reuse=is_reuse, sq=sq, cand=cand, k=int(k), fallback=fallback)
+    return dict(T=T, is_reuse=is_reuse, sq=sq, cand=cand, k=int(k), fallback=fallback,
+                overflow=np.flatnonzero(widened))
 
 
 # ---------------------------------------------------------------------------

@@ -192,6 +192,76 @@ def test_plan_request_brute_force_random():
         assert p["k"] == (num * len(cand)) // 100
 
 
+def test_plan_request_overflow_hand_cases():
+    """§3.3 second paragraph: one block of the reused neighbours on each side
+    of every non-reused interval joins the Sparse-Q set."""
+    pieces = [("reuse", 100), ("new", 20), ("reuse", 50), ("new", 10)]
+    p = oracle.plan_request(pieces, (1, 2), overflow_tokens=16)
+    assert not p["fallback"]
+    assert np.array_equal(p["overflow"], np.r_[84:100, 120:136, 154:170])
+    assert np.array_equal(p["sq"], np.r_[84:136, 154:180])
+    assert np.array_equal(p["cand"], np.r_[0:84, 136:154])
+    assert p["k"] == 51
+    # off by default: the same request without overflow
+    q = oracle.plan_request(pieces, (1, 2))
+    assert len(q["overflow"]) == 0 and np.array_equal(q["sq"], np.r_[100:120, 170:180])
+    # a reused piece shorter than two blocks between two new runs is taken whole
+    p = oracle.plan_request([("new", 5), ("reuse", 20), ("new", 5)], (1, 1), overflow_tokens=16)
+    assert np.array_equal(p["overflow"], np.r_[5:25]) and len(p["cand"]) == 0 and p["k"] == 0
+    # shorter than one block
+    p = oracle.plan_request([("reuse", 7), ("new", 3)], (1, 1), overflow_tokens=16)
+    assert np.array_equal(p["sq"], np.r_[0:10]) and p["k"] == 0
+    # overflow and the tail fallback overlap-free here; both join the Sparse-Q set
+    p = oracle.plan_request([("new", 10), ("reuse", 100)], (1, 2), overflow_tokens=16)
+    assert p["fallback"]
+    assert np.array_equal(p["overflow"], np.r_[10:26])
+    assert np.array_equal(p["sq"], np.r_[0:26, 46:110])
+    assert np.array_equal(p["cand"], np.r_[26:46]) and p["k"] == 10
+    # adjacent reused pieces: only the piece touching the new run gives a block
+    p = oracle.plan_request([("reuse", 40), ("reuse", 8), ("new", 4), ("reuse", 30)], (0, 1),
+                            overflow_tokens=16)
+    assert np.array_equal(p["overflow"], np.r_[40:48, 52:68])
+    # adjacent new pieces form one interval: no block between them
+    p = oracle.plan_request([("reuse", 40), ("new", 4), ("new", 6), ("reuse", 40), ("new", 1)],
+                            (0, 1), overflow_tokens=16)
+    assert np.array_equal(p["overflow"], np.r_[24:40, 50:66, 74:90])
+    with pytest.raises(ValueError):
+        oracle.plan_request(pieces, (1, 2), overflow_tokens=-1)
+
+
+def test_plan_request_overflow_brute_force_random():
+    """Dual formulation, token by token: a reused token is widened iff its
+    own piece borders a new piece on that side within one block."""
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        pieces = [(("reuse", "new")[rng.integers(2)], int(rng.integers(0, 60)))
+                  for _ in range(rng.integers(1, 8))]
+        B = int(rng.integers(1, 33))
+        num = int(rng.integers(0, 101))
+        p = oracle.plan_request(pieces, (num, 100), overflow_tokens=B)
+        kept = [pc for pc in pieces if pc[1] > 0]
+        toks, widened = [], set()
+        for i, (kind, n) in enumerate(kept):
+            t0 = len(toks)
+            toks += [kind] * n
+            if kind != "reuse":
+                continue
+            if i + 1 < len(kept) and kept[i + 1][0] == "new":
+                widened |= set(range(t0 + n - min(B, n), t0 + n))
+            if i > 0 and kept[i - 1][0] == "new":
+                widened |= set(range(t0, t0 + min(B, n)))
+        T = len(toks)
+        tail = set()
+        if kept and kept[-1][0] == "reuse":
+            tail = set(range(T - min(64, kept[-1][1]), T))
+        sq = sorted(set(i for i in range(T) if toks[i] == "new") | tail | widened)
+        cand = [i for i in range(T) if toks[i] == "reuse" and i not in tail | widened]
+        assert list(p["overflow"]) == sorted(widened)
+        assert list(p["sq"]) == sq
+        assert list(p["cand"]) == cand
+        assert p["k"] == (num * len(cand)) // 100
+
+
 # ------------------------------------------------------------ attention -----
 
 def _attn_triple_loop(q, q_pos, K, V):
