@@ -132,11 +132,16 @@ typedef struct {
 sx_status sx_rope_table(double theta, int32_t head_dim, int32_t n_pos, float *tab_h);
 
 /* Token classes and selection budgets of a batch (§3.2: the index sets
- * I_reuse and I_nr, and the tail fallback).
+ * I_reuse and I_nr, and the tail fallback; §3.3: overflow).
  *   Request r consists of pieces piece_start_h[r] .. piece_start_h[r+1]-1;
  *   piece p is piece_len_h[p] tokens, reused if piece_reuse_h[p] != 0.
  *   Empty pieces are ignored.  If a request's last token is reused, the last
  *   min(fallback_tokens, L) tokens of its final reused piece join I_nr.
+ *   Overflow (off when overflow_tokens is 0; one block = 16 tokens in the
+ *   paper's setting): for every run of new pieces, the last
+ *   min(overflow_tokens, L) tokens of the reused piece right before it and
+ *   the first min(overflow_tokens, L) tokens of the reused piece right after
+ *   it join I_nr too (the Sparse-Q interval widened by one block per side).
  * Outputs (host, caller-allocated):
  *   seq_start_h [n_req+1]        packed token offsets
  *   tok_class_h [n_tok_cap]      0 = selection candidate (reused, not in
@@ -147,13 +152,15 @@ sx_status sx_rope_table(double theta, int32_t head_dim, int32_t n_pos, float *ta
  *   n_cand_h    [n_req]          number of candidates R_r
  *   k_h         [n_req]          floor(ratio_num_h[r] * R_r / ratio_den_h[r])
  * The ratio is a fraction of the candidates in [0, 1].  Returns SX_EINVAL
- * for negative lengths, a ratio outside [0,1], a zero denominator, or a
- * batch longer than n_tok_cap tokens. */
+ * for negative lengths, a ratio outside [0,1], a zero denominator, a
+ * negative fallback_tokens or overflow_tokens, or a batch longer than
+ * n_tok_cap tokens. */
 sx_status sx_plan_layout(int32_t n_req, const int32_t *piece_start_h, const int32_t *piece_reuse_h,
                          const int32_t *piece_len_h, const int32_t *ratio_num_h,
-                         const int32_t *ratio_den_h, int32_t fallback_tokens, int32_t n_tok_cap,
-                         int32_t *seq_start_h, uint8_t *tok_class_h, int32_t *sq_rows_h,
-                         int32_t *sq_start_h, int32_t *n_cand_h, int32_t *k_h);
+                         const int32_t *ratio_den_h, int32_t fallback_tokens,
+                         int32_t overflow_tokens, int32_t n_tok_cap, int32_t *seq_start_h,
+                         uint8_t *tok_class_h, int32_t *sq_rows_h, int32_t *sq_start_h,
+                         int32_t *n_cand_h, int32_t *k_h);
 
 /* Split reused runs into page-granular realign jobs (§4.5: allocate fresh
  * blocks for hits, then copy-Delta-RoPE them).  Token j of run s comes from

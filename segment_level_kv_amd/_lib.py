@@ -72,7 +72,7 @@ def lib():
         P, I, Z, D = C.c_void_p, C.c_int32, C.c_size_t, C.c_double
         sig = {
             "sx_rope_table": (I, [D, I, I, P]),
-            "sx_plan_layout": (I, [I, P, P, P, P, P, I, I, P, P, P, P, P, P]),
+            "sx_plan_layout": (I, [I, P, P, P, P, P, I, I, I, P, P, P, P, P, P]),
             "sx_plan_realign": (I, [P, I, P, I, P, I, I, I, P, P, I, P]),
             "sx_realign_jobs_bound": (I, [P, I, I]),
             "sx_workspace_bytes": (Z, [I, P, I, I, I]),
@@ -131,7 +131,7 @@ def sx_rope_table(theta: float, head_dim: int, n_pos: int) -> np.ndarray:
     return tab
 
 
-def sx_plan_layout(requests, fallback_tokens: int = 64):
+def sx_plan_layout(requests, fallback_tokens: int = 64, overflow_tokens: int = 0):
     """requests: list of (pieces, (num, den)); pieces = [(is_reuse, length)].
 
     Returns dict of numpy arrays: seq_start, tok_class, sq_rows, sq_start,
@@ -156,7 +156,8 @@ def sx_plan_layout(requests, fallback_tokens: int = 64):
     n_cand = np.zeros(n_req, np.int32)
     k = np.zeros(n_req, np.int32)
     _check(lib().sx_plan_layout(n_req, _ptr(ps), _ptr(ru), _ptr(ln), _ptr(nu), _ptr(de),
-                                fallback_tokens, n_cap, _ptr(seq_start), _ptr(tok_class),
+                                fallback_tokens, overflow_tokens, n_cap, _ptr(seq_start),
+                                _ptr(tok_class),
                                 _ptr(sq_rows), _ptr(sq_start), _ptr(n_cand), _ptr(k)),
            "sx_plan_layout")
     n_tok = int(seq_start[-1])

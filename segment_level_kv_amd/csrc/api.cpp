@@ -122,14 +122,16 @@ sx_status sx_rope_table(double theta, int32_t head_dim, int32_t n_pos, float* ta
 
 sx_status sx_plan_layout(int32_t n_req, const int32_t* piece_start_h, const int32_t* piece_reuse_h,
                          const int32_t* piece_len_h, const int32_t* ratio_num_h,
-                         const int32_t* ratio_den_h, int32_t fallback_tokens, int32_t n_tok_cap,
-                         int32_t* seq_start_h, uint8_t* tok_class_h, int32_t* sq_rows_h,
-                         int32_t* sq_start_h, int32_t* n_cand_h, int32_t* k_h) {
+                         const int32_t* ratio_den_h, int32_t fallback_tokens,
+                         int32_t overflow_tokens, int32_t n_tok_cap, int32_t* seq_start_h,
+                         uint8_t* tok_class_h, int32_t* sq_rows_h, int32_t* sq_start_h,
+                         int32_t* n_cand_h, int32_t* k_h) {
   SX_REQUIRE(n_req >= 1, SX_EINVAL, "sx_plan_layout: n_req must be >= 1");
   SX_REQUIRE(piece_start_h && piece_reuse_h && piece_len_h && ratio_num_h && ratio_den_h &&
                  seq_start_h && tok_class_h && sq_rows_h && sq_start_h && n_cand_h && k_h,
              SX_EINVAL, "sx_plan_layout: NULL argument");
   SX_REQUIRE(fallback_tokens >= 0, SX_EINVAL, "sx_plan_layout: fallback_tokens < 0");
+  SX_REQUIRE(overflow_tokens >= 0, SX_EINVAL, "sx_plan_layout: overflow_tokens < 0");
   SX_REQUIRE(piece_start_h[0] == 0, SX_EINVAL, "sx_plan_layout: piece_start_h[0] must be 0");
   // validate everything before writing any output
   int64_t total = 0;
@@ -151,12 +153,30 @@ sx_status sx_plan_layout(int32_t n_req, const int32_t* piece_start_h, const int3
   for (int r = 0; r < n_req; ++r) {
     const int t0 = tok;
     int last_reuse_len = -1;   // length of the last non-empty piece if it is reused
+    int prev_kind = -1;        // previous non-empty piece: -1 none, 0 new, 1 reused
+    int prev_len = 0;
     for (int p = piece_start_h[r]; p < piece_start_h[r + 1]; ++p) {
       const int L = piece_len_h[p];
       if (L == 0) continue;
-      const uint8_t cls = piece_reuse_h[p] ? 0 : 1;
-      for (int j = 0; j < L; ++j) tok_class_h[tok++] = cls;
-      last_reuse_len = piece_reuse_h[p] ? L : -1;
+      const int kind = piece_reuse_h[p] ? 1 : 0;
+      const uint8_t cls = kind ? 0 : 1;
+      for (int j = 0; j < L; ++j) tok_class_h[tok + j] = cls;
+      // Overflow (§3.3): one block of each reused neighbour of a new run
+      // joins the Sparse-Q set -- the block ending at a new run's start and
+      // the block starting right after it.
+      if (overflow_tokens > 0 && prev_kind >= 0 && prev_kind != kind) {
+        if (kind == 0) {   // reused piece, then this new one
+          const int m = prev_len < overflow_tokens ? prev_len : overflow_tokens;
+          for (int j = tok - m; j < tok; ++j) tok_class_h[j] = 1;
+        } else {           // new run, then this reused piece
+          const int m = L < overflow_tokens ? L : overflow_tokens;
+          for (int j = tok; j < tok + m; ++j) tok_class_h[j] = 1;
+        }
+      }
+      tok += L;
+      prev_kind = kind;
+      prev_len = L;
+      last_reuse_len = kind ? L : -1;
     }
     if (last_reuse_len > 0) {   // tail fallback: last tokens of the final reused piece probe
       const int m = last_reuse_len < fallback_tokens ? last_reuse_len : fallback_tokens;

@@ -110,7 +110,8 @@ class SparseXLayerRun:
       attention       -- sx_sparse_attn(A) -> O
     """
 
-    def __init__(self, case, device="cuda", ratios=None, extra_guard_pages: int = 8):
+    def __init__(self, case, device="cuda", ratios=None, extra_guard_pages: int = 8,
+                 overflow_tokens: int = 0):
         import torch as _t
         from . import synth
         self.case = case
@@ -123,7 +124,7 @@ class SparseXLayerRun:
         ratios = ratios or [rq.ratio for rq in case.requests]
         reqs = [([(kind == "reuse", n) for kind, n in case.piece_lengths(r)], ratios[r])
                 for r in range(n_req)]
-        self.plan = L.sx_plan_layout(reqs)
+        self.plan = L.sx_plan_layout(reqs, overflow_tokens=overflow_tokens)
         seq_start = self.plan["seq_start"]
         self.n_tok = int(seq_start[-1])
         lens = np.diff(seq_start)

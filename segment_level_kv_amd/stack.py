@@ -23,13 +23,15 @@ class HybridStackRun:
 
     layout: list per request of pieces [("reuse", seg_id) | ("new", L)];
     seg_len / seg_p_src: per segment id, its length and the RoPE position of
-    its cached copy; ratios: per request (num, den).
+    its cached copy; ratios: per request (num, den); overflow_tokens: the
+    block of reused tokens on each side of a new run that joins the
+    Sparse-Q set (§3.3; 0 = off).
     inputs(l) must return (x [n_tok, hidden], w_qkv, x_cache [sum seg len,
     hidden] in segment-id order) as device tensors of the storage type.
     """
 
     def __init__(self, dims, n_layers: int, threshold: int, layout, seg_len, seg_p_src, ratios,
-                 inputs, device="cuda", page_seed: int = 7):
+                 inputs, device="cuda", page_seed: int = 7, overflow_tokens: int = 0):
         self.dims, self.cdims = dims, make_dims(dims)
         self.n_layers, self.t = n_layers, threshold
         self.device = device
@@ -47,7 +49,7 @@ class HybridStackRun:
                 start += n
             reqs.append((pl, ratios[r]))
             runs.append(rr)
-        self.plan = L.sx_plan_layout(reqs)
+        self.plan = L.sx_plan_layout(reqs, overflow_tokens=overflow_tokens)
         self.seq_start_h = self.plan["seq_start"]
         self.n_tok = int(self.seq_start_h[-1])
         lens = np.diff(self.seq_start_h)

@@ -228,6 +228,19 @@ def llama_layer_case(seed: int = 1002, ratio=(15, 100), n_seg: int = 8, seg_len:
                      p_src_max=8192, cache_noise=cache_noise)
 
 
+def interleaved_case(seed: int = 1005, ratio=(20, 100), dims: Dims = LLAMA8B) -> LayerCase:
+    """Two requests whose new runs sit between reused segments (the layout
+    the overflow blocks of §3.3 are meant for), sharing segments 1 and 3:
+      r0: new 40 | seg0 300 | new 24 | seg1 200 | seg2 20 | new 8 | seg3 150
+      r1: seg3 150 | new 5 | seg1 200 | new 33
+    r0 ends on a reused segment (tail fallback), r1 on new tokens."""
+    lay0 = [("new", 40), ("reuse", 0), ("new", 24), ("reuse", 1), ("reuse", 2), ("new", 8),
+            ("reuse", 3)]
+    lay1 = [("reuse", 3), ("new", 5), ("reuse", 1), ("new", 33)]
+    return make_case("interleaved", dims, [300, 200, 20, 150], [lay0, lay1], [ratio, ratio],
+                     seed, p_src_max=4096)
+
+
 def rag_layout(n_passages: int = 16, system: int = 512, passage: int = 1920, query: int = 256):
     """RAG mix: reused system segment + reused passages + new query.
 

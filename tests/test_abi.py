@@ -118,8 +118,9 @@ def test_rope_table_matches_float64_angles():
         L.sx_rope_table(-1.0, 128, 10)
 
 
-def test_plan_layout_matches_oracle_random_batches():
-    rng = np.random.default_rng(5)
+@pytest.mark.parametrize("overflow", [0, 16, 5])
+def test_plan_layout_matches_oracle_random_batches(overflow):
+    rng = np.random.default_rng(5 + overflow)
     for _ in range(100):
         n_req = int(rng.integers(1, 5))
         reqs, pieces_list, ratios = [], [], []
@@ -130,10 +131,10 @@ def test_plan_layout_matches_oracle_random_batches():
             pieces_list.append(pieces)
             ratios.append(ratio)
             reqs.append(([(k == "reuse", n) for k, n in pieces], ratio))
-        got = L.sx_plan_layout(reqs)
+        got = L.sx_plan_layout(reqs, overflow_tokens=overflow)
         off = 0
         for r in range(n_req):
-            ref = oracle.plan_request(pieces_list[r], ratios[r])
+            ref = oracle.plan_request(pieces_list[r], ratios[r], overflow_tokens=overflow)
             T = ref["T"]
             assert got["seq_start"][r + 1] - got["seq_start"][r] == T
             cls = got["tok_class"][off:off + T]
@@ -150,6 +151,8 @@ def test_plan_layout_rejects_bad_ratio():
         L.sx_plan_layout([([(True, 10)], (3, 2))])
     with pytest.raises(L.SxError):
         L.sx_plan_layout([([(True, 10)], (1, 0))])
+    with pytest.raises(L.SxError):
+        L.sx_plan_layout([([(True, 10)], (1, 2))], overflow_tokens=-1)
 
 
 def test_plan_realign_covers_every_token_once():

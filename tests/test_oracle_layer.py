@@ -60,9 +60,9 @@ def _build_caches(case, r, pos_shift=0):
     return segs
 
 
-def _run(case, ratio, r=0, pos_shift=0, **kw):
+def _run(case, ratio, r=0, pos_shift=0, overflow=0, **kw):
     d = case.dims
-    plan = oracle.plan_request(case.piece_lengths(r), ratio)
+    plan = oracle.plan_request(case.piece_lengths(r), ratio, overflow_tokens=overflow)
     segs = _build_caches(case, r, pos_shift)
     return plan, oracle.sparse_layer(case.request_x(r), case.wq, case.wk, case.wv, plan, segs,
                                      d.theta, d.n_q_heads, d.n_kv_heads, d.head_dim, d.dtype,
@@ -105,12 +105,17 @@ def test_ratio_100_is_full_prefill(dims, noise):
 
 
 @pytest.mark.parametrize("dims", [SMALL_BF16, SMALL_F32])
-def test_ratio_0_is_plain_reuse_with_realignment(dims):
+@pytest.mark.parametrize("overflow", [0, 16])
+def test_ratio_0_is_plain_reuse_with_realignment(dims, overflow):
     """Pin P6: no candidate selected => only the new tokens get outputs, over
-    the cached K rotated to the new positions and the cached V."""
+    the cached K rotated to the new positions and the cached V.  With
+    overflow, the 16-token blocks around each new run (§3.3) are recomputed
+    and attend like the new tokens."""
     case = _case(dims, LAYOUT, LENS, noise=0.5)
-    plan, out = _run(case, (0, 1))
+    plan, out = _run(case, (0, 1), overflow=overflow)
     assert np.array_equal(out["A"], plan["sq"]) and len(out["S"]) == 0
+    if overflow:   # reuse 0..47 | new 48..59 | reuse 60..91 | reuse 92..131 | new 132..151
+        assert np.array_equal(plan["sq"], np.r_[32:76, 116:152])
     # straight computation: complex rotation by (new - old) of the stored cache
     x = case.request_x(0)
     T = x.shape[0]
@@ -202,3 +207,15 @@ def test_fallback_rows_probe_and_get_outputs():
     assert plan["fallback"] and np.array_equal(plan["sq"], np.arange(80, 144))
     assert plan["k"] == 20 and len(out["S"]) == 20 and np.all(out["S"] < 80)
     assert np.isclose(out["scores"].sum(), 64 * 4)
+
+
+@pytest.mark.parametrize("dims", [SMALL_BF16, SMALL_F32])
+def test_overflow_covering_every_reused_piece_is_full_prefill(dims):
+    """Every reused piece of LAYOUT borders a new run; with blocks as long as
+    the longest piece, overflow alone (ratio 0) recomputes every token, so the
+    layer equals a full prefill."""
+    case = _case(dims, LAYOUT, LENS, noise=0.5)
+    plan, out = _run(case, (0, 1), overflow=max(LENS))
+    assert len(out["A"]) == plan["T"] and plan["k"] == 0
+    ref = _straight_full_prefill(case)
+    assert np.max(np.abs(out["O_exact"] - ref)) < 1e-9

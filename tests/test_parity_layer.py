@@ -24,9 +24,9 @@ from tests.gpu_util import (BF16_STEP_REL, assert_close_bf16, assert_close_f32, 
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_request(case, r, ratio):
+def _oracle_request(case, r, ratio, overflow=0):
     d = case.dims
-    plan = oracle.plan_request(case.piece_lengths(r), ratio)
+    plan = oracle.plan_request(case.piece_lengths(r), ratio, overflow_tokens=overflow)
     segs = []
     for dst, sid in case.reuse_runs(r):
         sg = case.segments[sid]
@@ -39,10 +39,11 @@ def _oracle_request(case, r, ratio):
     return plan, out
 
 
-def _check_case(case, ratios=None):
+def _check_case(case, ratios=None, overflow=0):
     d = case.dims
-    say(f"[layer] case={case.name} dtype={d.dtype} requests={len(case.requests)}")
-    run = SparseXLayerRun(case, ratios=ratios).run()
+    say(f"[layer] case={case.name} dtype={d.dtype} requests={len(case.requests)} "
+        f"overflow={overflow}")
+    run = SparseXLayerRun(case, ratios=ratios, overflow_tokens=overflow).run()
     torch.cuda.synchronize()
     guard_before = None
     seq = run.plan["seq_start"]
@@ -54,7 +55,7 @@ def _check_case(case, ratios=None):
     sel_off, act_off = 0, 0
     for r in range(len(case.requests)):
         ratio = (ratios or [rq.ratio for rq in case.requests])[r]
-        plan, ref = _oracle_request(case, r, ratio)
+        plan, ref = _oracle_request(case, r, ratio, overflow)
         T = plan["T"]
         k = plan["k"]
         assert k == k_all[r]
@@ -123,3 +124,19 @@ def test_layer_agent_batch_fallback_bf16():
     """Several requests, no new tokens: the tail fallback supplies I_nr."""
     case = synth.agent_case(n_req=3, target=2500, n_pool=10, lmax=512)
     _check_case(case)
+
+
+@pytest.mark.parametrize("overflow", [0, 16])
+def test_layer_interleaved_overflow_bf16(overflow):
+    """New runs between reused segments, two requests; with overflow the
+    16-token blocks around every new run are recomputed, probe and attend."""
+    case = synth.interleaved_case()
+    run = _check_case(case, overflow=overflow)
+    if overflow:
+        seq = run.plan["seq_start"]
+        for r in range(len(case.requests)):
+            ref = oracle.plan_request(case.piece_lengths(r), case.requests[r].ratio,
+                                      overflow_tokens=overflow)
+            assert len(ref["overflow"]) > 0
+            act = run.act_rows.cpu().numpy()
+            assert np.isin(ref["overflow"] + seq[r], act).all()
