@@ -14,7 +14,8 @@
  * ---------------------------------------
  * - Pointers are DEVICE pointers unless the parameter name ends in `_h`
  *   (host memory).  The caller owns every buffer; the library allocates and
- *   frees nothing and keeps no state between calls.
+ *   frees nothing and keeps no state between calls -- except the segment
+ *   index (sx_index_*), a host object the caller creates and destroys.
  * - Every compute call enqueues its kernels on `stream` (a hipStream_t; NULL
  *   is the null stream) and returns without synchronising.  Results are
  *   valid in stream order.
@@ -59,7 +60,8 @@ typedef enum {
   SX_EINVAL = -1,        /* bad pointer, size or inconsistent argument      */
   SX_EUNSUPPORTED = -2,  /* valid but not implemented (e.g. head_dim 96)    */
   SX_EWORKSPACE = -3,    /* workspace missing or smaller than required      */
-  SX_EDEVICE = -4        /* a HIP call or kernel launch failed              */
+  SX_EDEVICE = -4,       /* a HIP call or kernel launch failed              */
+  SX_ENOMEM = -5         /* the block pool cannot supply the blocks asked for */
 } sx_status;
 
 typedef enum { SX_F32 = 0, SX_BF16 = 1 } sx_dtype;
@@ -178,6 +180,88 @@ sx_status sx_plan_realign(const sx_segment *segs_h, int32_t n_segs, const int32_
 
 /* Upper bound on the job count sx_plan_realign() produces. */
 int32_t sx_realign_jobs_bound(const sx_segment *segs_h, int32_t n_segs, int32_t page_size);
+
+/* ----------------------------------------------------------------------- */
+/* Segment lookup (host; §4.1-§4.5).  Turns a reused segment's token ids    */
+/* and extra key into cached blocks and realign descriptors.                */
+/* ----------------------------------------------------------------------- */
+
+/* h_virt = H(B, e) of §4.3 for the n_tok token ids of a block and an extra
+ * key e: SHA-256 (FIPS 180-4) over e as 8 little-endian bytes followed by
+ * each token id as 4 little-endian bytes; *hash_h = the first 8 digest bytes
+ * as a little-endian integer.  Position- and prefix-independent (§4.4): no
+ * parent hash is chained in. */
+sx_status sx_virtual_hash(const int32_t *tokens_h, int32_t n_tok, uint64_t extra_key,
+                          uint64_t *hash_h);
+
+/* The block pool and its virtual-block index (§4.1 frozen blocks, §4.2 the
+ * frozen-block pool, §4.4 virtual blocks).  One pool of n_blocks physical
+ * KV blocks (the page ids of sx_pages) of block_size tokens.  Per block:
+ * in use or free, a reference count, a frozen flag and a hit count.  A
+ * virtual entry {h_virt, block, position of its first token in the cached
+ * copy, its token ids, extra key} owns no KV memory.  Frozen blocks stay in
+ * use at reference count 0; when more than evict_num/evict_den of the pool
+ * is in use after an allocation (§4.1: 90% -> 9/10), frozen blocks nobody
+ * holds are evicted, fewest hits first, then the earliest frozen, then the
+ * lowest id.  Not thread-safe: calls on one index must not overlap.  Calls
+ * that take a list of ids check the whole list first; a failed call leaves
+ * the index unchanged.  *index_h is NULL on failure. */
+typedef struct sx_index sx_index;
+sx_status sx_index_create(int32_t n_blocks, int32_t block_size, int32_t evict_num,
+                          int32_t evict_den, sx_index **index_h);
+void sx_index_destroy(sx_index *index);
+
+/* Allocate n blocks (the lowest free ids, ascending, reference count 1) into
+ * ids_h [n]: a request's carrier blocks (§4.5) or a segment being cached.
+ * Evicts unheld frozen blocks when fewer than n are free; SX_ENOMEM if even
+ * that cannot supply n.  Then evicts while the pool is above the threshold. */
+sx_status sx_index_alloc(sx_index *index, int32_t n, int32_t *ids_h);
+
+/* Drop one reference per listed id (an id may repeat).  A block that reaches
+ * 0 and is not frozen is freed with its virtual entries.  SX_EINVAL if a
+ * block is free or would drop below 0. */
+sx_status sx_index_release(sx_index *index, const int32_t *ids_h, int32_t n);
+
+/* Register a cached segment (§4.2 insert API; §4.4): its n_tok token ids
+ * tokens_h, extra key, the ceil(n_tok / block_size) blocks ids_h holding it
+ * (all in use) and p_src, the RoPE position of its first token in that
+ * copy.  Every full block j gets a virtual entry at position
+ * p_src + j*block_size; the partial last block gets none.  frozen != 0 also
+ * freezes the full blocks. */
+sx_status sx_index_insert(sx_index *index, const int32_t *tokens_h, int32_t n_tok,
+                          uint64_t extra_key, const int32_t *ids_h, int32_t p_src, int32_t frozen);
+
+/* Look up the n_tok / block_size full blocks of a reused segment (§4.3,
+ * §4.5): block j hits a live entry whose hash, extra key and token ids all
+ * equal its own (the most recently inserted of several).  Writes block_h[j]
+ * (the physical block) and pos_h[j] (its cached position), or -1 / -1 on a
+ * miss.  Each hit takes a reference on its block, to be released once the
+ * realign copy out of it is done, and counts one hit. */
+sx_status sx_index_lookup(sx_index *index, const int32_t *tokens_h, int32_t n_tok,
+                          uint64_t extra_key, int32_t *block_h, int32_t *pos_h);
+
+/* Delete blocks from the index (§4.2 delete API): their virtual entries go,
+ * they are unfrozen, and those nobody holds are freed. */
+sx_status sx_index_remove(sx_index *index, const int32_t *ids_h, int32_t n);
+
+/* stats_h[4] = {blocks in use, free blocks, frozen blocks, live entries}. */
+sx_status sx_index_stats(const sx_index *index, int32_t *stats_h);
+
+/* Realign descriptors of one reused piece from its lookup (§4.5).  The piece
+ * is n_tok tokens at token index dst_start of request req; block_h/pos_h
+ * hold the lookup of its n_tok / block_size full blocks.  Each run of hits
+ * whose cached positions continue block after block becomes one sx_segment
+ * (src_slot0 0, src_pages_off = ids_off + its first id's index in src_ids_h);
+ * src_ids_h receives the hit blocks in order.  piece_reuse_h/piece_len_h
+ * receive the piece's split into reused (1) and to-prefill (0) runs -- misses
+ * and the partial last block -- in sx_plan_layout's piece format.  Each
+ * output array needs n_tok / block_size + 1 entries; counts go to
+ * *n_segs_h, *n_ids_h and *n_pieces_h. */
+sx_status sx_plan_segments(int32_t req, int32_t dst_start, const int32_t *block_h,
+                           const int32_t *pos_h, int32_t n_tok, int32_t block_size,
+                           int32_t ids_off, sx_segment *segs_h, int32_t *n_segs_h,
+                           int32_t *src_ids_h, int32_t *n_ids_h, int32_t *piece_reuse_h,
+                           int32_t *piece_len_h, int32_t *n_pieces_h);
 
 /* ----------------------------------------------------------------------- */
 /* Device entry points.                                                     */

@@ -54,6 +54,8 @@ class BlockIndex:
         lookup hits; ties go to the block frozen earliest, then the lower
         id.
       - Evicting a frozen block drops its virtual entries and frees it.
+      - Calls taking a list of ids check the whole list before changing
+        anything, so a failed call leaves the index as it was.
       - release(ids) drops one reference per id; an unfrozen block whose
         count reaches 0 is freed and its virtual entries dropped (an
         ordinary block returns to the free list, §4.1); a frozen block stays.
@@ -130,9 +132,11 @@ class BlockIndex:
         return ids
 
     def release(self, ids):
+        ids = [int(b) for b in ids]
+        for b in ids:      # validate the whole list first: an error changes nothing
+            if not (0 <= b < self.n) or not self.used[b] or ids.count(b) > self.ref[b]:
+                raise ValueError(f"block {b} is not held that often")
         for b in ids:
-            if not (0 <= b < self.n) or not self.used[b] or self.ref[b] <= 0:
-                raise ValueError(f"block {b} is not held")
             self.ref[b] -= 1
             if self.ref[b] == 0 and not self.frozen[b]:
                 self._free(b)
@@ -175,9 +179,13 @@ class BlockIndex:
         return blocks, pos
 
     def remove(self, ids):
-        for b in ids:
+        ids = [int(b) for b in ids]
+        for b in ids:      # validate the whole list first: an error changes nothing
             if not (0 <= b < self.n) or not self.used[b]:
                 raise ValueError(f"block {b} is not in use")
+        for b in ids:
+            if not self.used[b]:
+                continue   # listed twice and freed by its first mention
             self._drop_entries(b)
             self.frozen[b] = False
             if self.ref[b] == 0:

@@ -16,7 +16,7 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsx.so")
 
-SX_OK, SX_EINVAL, SX_EUNSUPPORTED, SX_EWORKSPACE, SX_EDEVICE = 0, -1, -2, -3, -4
+SX_OK, SX_EINVAL, SX_EUNSUPPORTED, SX_EWORKSPACE, SX_EDEVICE, SX_ENOMEM = 0, -1, -2, -3, -4, -5
 SX_F32, SX_BF16 = 0, 1
 SX_OP_REALIGN, SX_OP_RECOMPUTE, SX_OP_SELECT, SX_OP_TOPK, SX_OP_SPARSE_ATTN, SX_OP_FULL_ATTN = range(6)
 
@@ -24,6 +24,8 @@ EXPORTED = [
     "sx_rope_table", "sx_plan_layout", "sx_plan_realign", "sx_realign_jobs_bound",
     "sx_workspace_bytes", "sx_rope_realign", "sx_recompute_kv", "sx_select_topk", "sx_topk",
     "sx_sparse_attn", "sx_full_attn", "sx_last_error",
+    "sx_virtual_hash", "sx_index_create", "sx_index_destroy", "sx_index_alloc", "sx_index_release",
+    "sx_index_insert", "sx_index_lookup", "sx_index_remove", "sx_index_stats", "sx_plan_segments",
 ]
 
 
@@ -69,7 +71,7 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m segment_level_kv_amd.build`")
         L = C.CDLL(LIB_PATH)
-        P, I, Z, D = C.c_void_p, C.c_int32, C.c_size_t, C.c_double
+        P, I, Z, D, U = C.c_void_p, C.c_int32, C.c_size_t, C.c_double, C.c_uint64
         sig = {
             "sx_rope_table": (I, [D, I, I, P]),
             "sx_plan_layout": (I, [I, P, P, P, P, P, I, I, I, P, P, P, P, P, P]),
@@ -83,6 +85,16 @@ def lib():
             "sx_sparse_attn": (I, [P, P, P, P, P, I, P, P, P, P, Z, P]),
             "sx_full_attn": (I, [P, P, P, P, P, P, P, Z, P]),
             "sx_last_error": (C.c_char_p, []),
+            "sx_virtual_hash": (I, [P, I, U, P]),
+            "sx_index_create": (I, [I, I, I, I, P]),
+            "sx_index_destroy": (None, [P]),
+            "sx_index_alloc": (I, [P, I, P]),
+            "sx_index_release": (I, [P, P, I]),
+            "sx_index_insert": (I, [P, P, I, U, P, I, I]),
+            "sx_index_lookup": (I, [P, P, I, U, P, P]),
+            "sx_index_remove": (I, [P, P, I]),
+            "sx_index_stats": (I, [P, P]),
+            "sx_plan_segments": (I, [I, I, P, P, I, I, I, P, P, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -163,6 +175,89 @@ def sx_plan_layout(requests, fallback_tokens: int = 64, overflow_tokens: int = 0
     n_tok = int(seq_start[-1])
     return dict(seq_start=seq_start, tok_class=tok_class[:n_tok], sq_rows=sq_rows[:sq_start[-1]],
                 sq_start=sq_start, n_cand=n_cand, k=k)
+
+
+def _i32(v):
+    return np.ascontiguousarray(np.asarray(v, dtype=np.int32).reshape(-1))
+
+
+def sx_virtual_hash(tokens, extra_key: int) -> int:
+    t = _i32(tokens)
+    out = np.zeros(1, np.uint64)
+    _check(lib().sx_virtual_hash(_ptr(t), len(t), int(extra_key), _ptr(out)), "sx_virtual_hash")
+    return int(out[0])
+
+
+class SegmentIndex:
+    """Owner of one sx_index (the block pool and its virtual-block index)."""
+
+    def __init__(self, n_blocks: int, block_size: int = 16, evict_num: int = 9,
+                 evict_den: int = 10):
+        h = C.c_void_p()
+        _check(lib().sx_index_create(n_blocks, block_size, evict_num, evict_den, C.byref(h)),
+               "sx_index_create")
+        self._h = h
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            lib().sx_index_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc(self, n: int) -> list:
+        ids = np.zeros(max(n, 1), np.int32)
+        _check(lib().sx_index_alloc(self._h, n, _ptr(ids)), "sx_index_alloc")
+        return ids[:n].tolist()
+
+    def release(self, ids):
+        a = _i32(ids)
+        _check(lib().sx_index_release(self._h, _ptr(a), len(a)), "sx_index_release")
+
+    def insert(self, tokens, extra_key: int, ids, p_src: int, frozen: bool):
+        t, a = _i32(tokens), _i32(ids)
+        _check(lib().sx_index_insert(self._h, _ptr(t), len(t), int(extra_key), _ptr(a), p_src,
+                                     1 if frozen else 0), "sx_index_insert")
+
+    def lookup(self, tokens, extra_key: int):
+        t = _i32(tokens)
+        nb = len(t) // self.block_size
+        blk, pos = np.zeros(max(nb, 1), np.int32), np.zeros(max(nb, 1), np.int32)
+        _check(lib().sx_index_lookup(self._h, _ptr(t), len(t), int(extra_key), _ptr(blk),
+                                     _ptr(pos)), "sx_index_lookup")
+        return blk[:nb].tolist(), pos[:nb].tolist()
+
+    def remove(self, ids):
+        a = _i32(ids)
+        _check(lib().sx_index_remove(self._h, _ptr(a), len(a)), "sx_index_remove")
+
+    def stats(self):
+        st = np.zeros(4, np.int32)
+        _check(lib().sx_index_stats(self._h, _ptr(st)), "sx_index_stats")
+        return tuple(int(x) for x in st)
+
+
+def sx_plan_segments(req: int, dst_start: int, blocks, pos, n_tok: int, block_size: int = 16,
+                     ids_off: int = 0):
+    """Returns (segments as dicts, src_ids list, pieces [(is_reuse, L)])."""
+    b, p = _i32(blocks), _i32(pos)
+    cap = n_tok // block_size + 1
+    segs = (Segment * cap)()
+    ids = np.zeros(cap, np.int32)
+    reuse, lens = np.zeros(cap, np.int32), np.zeros(cap, np.int32)
+    ns, ni, npc = C.c_int32(), C.c_int32(), C.c_int32()
+    _check(lib().sx_plan_segments(req, dst_start, _ptr(b) if len(b) else None,
+                                  _ptr(p) if len(p) else None, n_tok, block_size, ids_off, segs,
+                                  C.byref(ns), _ptr(ids), C.byref(ni), _ptr(reuse), _ptr(lens),
+                                  C.byref(npc)), "sx_plan_segments")
+    out = [dict(req=s.req, dst_start=s.dst_start, len=s.len, p_src=s.p_src, src_slot0=s.src_slot0,
+                src_pages_off=s.src_pages_off) for s in segs[:ns.value]]
+    return out, ids[:ni.value].tolist(), [(bool(reuse[i]), int(lens[i])) for i in range(npc.value)]
 
 
 def sx_plan_realign(segments, src_page_ids: np.ndarray, block_table: np.ndarray,

@@ -29,7 +29,8 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
 ]
-SOURCES = ["api.cpp", "rope_realign.hip", "recompute_kv.hip", "attention.hip", "select.hip"]
+SOURCES = ["api.cpp", "seg_index.cpp", "rope_realign.hip", "recompute_kv.hip", "attention.hip",
+           "select.hip"]
 # Per-source extra flags.  The attention softmax never produces NaN (masked
 # logits are -inf), so max reductions need no NaN quieting.  Compiler-selected
 # MFMAs in attention write VGPRs (the score tiles the softmax reads); the
