@@ -71,6 +71,41 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
+def decode_measure(run, dims, n_layers: int, t: int, reps: int = 5):
+    """Decode attention of the request's last token over each sparse layer's
+    mixed cache after the prefill (sx_decode_attn), outside the timed prefill
+    steps.  Every layer has its own 64 MB K + 64 MB V pool, so a pass over the
+    sparse layers streams 3.6 GB and no layer's cache is still on chip when it
+    is read again.  Bytes per call: K and V of all tokens and kv heads, plus
+    q and o."""
+    import torch
+    T = run.n_tok
+    hq, hkv, d = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    q = torch.randn((1, hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    o = torch.empty((1, hq * d), dtype=torch.bfloat16, device="cuda")
+    layers = list(range(t, n_layers))
+    for l in layers:
+        run.decode_attention(l, q, o)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        for l in layers:
+            run.decode_attention(l, q, o)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (reps * len(layers))
+    nbytes = 2.0 * T * hkv * d * 2 + 2.0 * 2 * hq * d
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "sx_decode_attn (decode_fwd + decode_merge)", "tokens": T,
+            "us_per_call": round(us, 2), "bytes_per_call": nbytes, "achieved_GBps": round(gbs, 1),
+            "peak_GBps": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "calls_timed": reps * len(layers)}
+
+
 def cpu_baseline(dims, plan, n_sparse: int, T: int, reused: int, seed: int = 4242):
     """The float64 oracle on a bounded sample of one sparse layer of the same
     workload, scaled to tokens/s per layer.  Sample: realign of one
@@ -250,6 +285,7 @@ def main():
         "full_layer_ms": round(full_rec_ms + full_attn_ms, 4),
         "wall_s_timed": round(wall, 3),
     }
+    out["decode_attn"] = decode_measure(run, dims, n_layers, t)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(dims, run.plan, n_sparse, T, reused)
     print(json.dumps(out), flush=True)

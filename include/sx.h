@@ -9,6 +9,8 @@
  *   3. Sparse-KV recomputation: gather, QKV GEMM, RoPE, scatter    (§3.4)
  *   4. causal GQA attention of the active rows over the mixed
  *      paged cache; full causal prefill before the threshold      (§3.4, §4.5)
+ * and around it the segment lookup that finds the reused blocks (§4.1-§4.5)
+ * and decode attention over the mixed cache afterwards (§4.5).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -269,7 +271,7 @@ sx_status sx_plan_segments(int32_t req, int32_t dst_start, const int32_t *block_
 
 /* Operation ids for sx_workspace_bytes(). */
 enum { SX_OP_REALIGN = 0, SX_OP_RECOMPUTE = 1, SX_OP_SELECT = 2, SX_OP_TOPK = 3,
-       SX_OP_SPARSE_ATTN = 4, SX_OP_FULL_ATTN = 5 };
+       SX_OP_SPARSE_ATTN = 4, SX_OP_FULL_ATTN = 5, SX_OP_DECODE = 6 };
 
 /* Bytes of device workspace `op` needs (0 if none).  n_tok: tokens of the
  * batch; n_rows: rows of the call (Sparse-Q rows for SX_OP_SELECT, active
@@ -361,6 +363,20 @@ sx_status sx_sparse_attn(const sx_dims *dims, const sx_layout *lay, const void *
 sx_status sx_full_attn(const sx_dims *dims, const sx_layout *lay, const void *q,
                        const sx_pages *kv, void *o, float *lse, void *ws, size_t ws_bytes,
                        void *stream);
+
+/* Decode attention over the mixed paged cache (§4.5 last paragraph: after
+ * the first prefill pass, decode reads the realigned and recomputed blocks
+ * through the block table).  One query row per request, at its last token:
+ * request r holds T_r = seq_start[r+1] - seq_start[r] tokens in its pages,
+ * the new token's k/v already written (sx_recompute_kv of that row), and
+ *   o[r][h*d:(h+1)*d] = sum_{j<T_r} softmax_j(q[r][h] . k_j^g / sqrt(d)) v_j^g
+ * with g = h / (Hq/Hkv).  q: [n_req][Hq][d]; o: [n_req][Hq*d]; lse (may be
+ * NULL): [n_req][Hq] natural-log normalisers.  A request with no tokens
+ * gets o = 0 and lse = -inf.  bf16 only (SX_EUNSUPPORTED for fp32).
+ * ws: sx_workspace_bytes(SX_OP_DECODE, dims, n_tok, 0, n_req) bytes. */
+sx_status sx_decode_attn(const sx_dims *dims, const sx_layout *lay, const void *q,
+                         const sx_pages *kv, void *o, float *lse, void *ws, size_t ws_bytes,
+                         void *stream);
 
 /* Text of the last non-OK status returned on the calling thread. */
 const char *sx_last_error(void);

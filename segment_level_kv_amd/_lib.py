@@ -18,12 +18,12 @@ LIB_PATH = os.path.join(_PKG, "libsx.so")
 
 SX_OK, SX_EINVAL, SX_EUNSUPPORTED, SX_EWORKSPACE, SX_EDEVICE, SX_ENOMEM = 0, -1, -2, -3, -4, -5
 SX_F32, SX_BF16 = 0, 1
-SX_OP_REALIGN, SX_OP_RECOMPUTE, SX_OP_SELECT, SX_OP_TOPK, SX_OP_SPARSE_ATTN, SX_OP_FULL_ATTN = range(6)
+SX_OP_REALIGN, SX_OP_RECOMPUTE, SX_OP_SELECT, SX_OP_TOPK, SX_OP_SPARSE_ATTN, SX_OP_FULL_ATTN, SX_OP_DECODE = range(7)
 
 EXPORTED = [
     "sx_rope_table", "sx_plan_layout", "sx_plan_realign", "sx_realign_jobs_bound",
     "sx_workspace_bytes", "sx_rope_realign", "sx_recompute_kv", "sx_select_topk", "sx_topk",
-    "sx_sparse_attn", "sx_full_attn", "sx_last_error",
+    "sx_sparse_attn", "sx_full_attn", "sx_decode_attn", "sx_last_error",
     "sx_virtual_hash", "sx_index_create", "sx_index_destroy", "sx_index_alloc", "sx_index_release",
     "sx_index_insert", "sx_index_lookup", "sx_index_remove", "sx_index_stats", "sx_plan_segments",
 ]
@@ -84,6 +84,7 @@ def lib():
             "sx_topk": (I, [P, P, P, I, I, P, P, P, Z, P]),
             "sx_sparse_attn": (I, [P, P, P, P, P, I, P, P, P, P, Z, P]),
             "sx_full_attn": (I, [P, P, P, P, P, P, P, Z, P]),
+            "sx_decode_attn": (I, [P, P, P, P, P, P, P, Z, P]),
             "sx_last_error": (C.c_char_p, []),
             "sx_virtual_hash": (I, [P, I, U, P]),
             "sx_index_create": (I, [I, I, I, I, P]),
@@ -323,6 +324,12 @@ def sx_sparse_attn(dims: Dims, lay: Layout, q, rows, row_start, n_rows: int, kv:
     _check(lib().sx_sparse_attn(_ref(dims), _ref(lay), _ptr(q), _ptr(rows), _ptr(row_start),
                                 n_rows, _ref(kv), _ptr(o), _ptr(lse), _ptr(ws), ws_bytes,
                                 _stream(stream)), "sx_sparse_attn")
+
+
+def sx_decode_attn(dims: Dims, lay: Layout, q, kv: Pages, o, lse, ws, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sx_decode_attn(_ref(dims), _ref(lay), _ptr(q), _ref(kv), _ptr(o), _ptr(lse),
+                                _ptr(ws), ws_bytes, _stream(stream)), "sx_decode_attn")
 
 
 def sx_full_attn(dims: Dims, lay: Layout, q, kv: Pages, o, lse, ws, stream=None):

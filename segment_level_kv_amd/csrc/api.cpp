@@ -258,6 +258,7 @@ size_t sx_workspace_bytes(int32_t op, const sx_dims* dims, int32_t n_tok, int32_
     case SX_OP_TOPK: return topk_ws_bytes(n_tok, n_req);
     case SX_OP_SPARSE_ATTN: return attn_ws_bytes(*dims, n_rows, n_req, true);
     case SX_OP_FULL_ATTN: return attn_ws_bytes(*dims, n_tok, n_req, true);
+    case SX_OP_DECODE: return decode_ws_bytes(*dims, n_tok, n_req);
     default: return 0;
   }
 }
@@ -318,6 +319,21 @@ sx_status sx_full_attn(const sx_dims* dims, const sx_layout* lay, const void* q,
              "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : (size_t)0);
   return launch_attention(*dims, *lay, q, nullptr, nullptr, lay->seq_start, lay->n_tok, *kv, o, lse,
                           ws, as_stream(stream));
+}
+
+sx_status sx_decode_attn(const sx_dims* dims, const sx_layout* lay, const void* q,
+                         const sx_pages* kv, void* o, float* lse, void* ws, size_t ws_bytes,
+                         void* stream) {
+  const char* fn = "sx_decode_attn";
+  SX_TRY(check_dims(dims, fn));
+  SX_REQUIRE(dims->dtype == SX_BF16, SX_EUNSUPPORTED, "%s: only the bf16 path is built", fn);
+  SX_TRY(check_layout(lay, fn));
+  SX_TRY(check_pages(kv, fn, "kv"));
+  SX_REQUIRE(q && o, SX_EINVAL, "%s: q/o is NULL", fn);
+  const size_t need = sx_workspace_bytes(SX_OP_DECODE, dims, lay->n_tok, 0, lay->n_req);
+  SX_REQUIRE(ws && ws_bytes >= need, SX_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn,
+             need, ws ? ws_bytes : (size_t)0);
+  return launch_decode(*dims, *lay, q, *kv, o, lse, ws, as_stream(stream));
 }
 
 sx_status sx_topk(const float* scores, const uint8_t* tok_class, const int32_t* seq_start,

@@ -43,6 +43,11 @@ sx_status launch_attention(const sx_dims& dims, const sx_layout& lay, const void
                            const int32_t* row_start, int n_rows, const sx_pages& kv, void* o,
                            float* lse, void* ws, hipStream_t stream);
 
+// Decode attention: one query row per request (its last token), bf16 only.
+size_t decode_ws_bytes(const sx_dims& d, int n_tok, int n_req);
+sx_status launch_decode(const sx_dims& dims, const sx_layout& lay, const void* q, const sx_pages& kv,
+                        void* o, float* lse, void* ws, hipStream_t stream);
+
 // Per-(kv head, token) partial attention-mass scores of the Sparse-Q rows.
 sx_status launch_scores(const sx_dims& dims, const sx_layout& lay, const void* q,
                         const int32_t* q_index, const int32_t* sq_rows, const int32_t* sq_start,

@@ -183,6 +183,13 @@ class HybridStackRun:
             L.sx_sparse_attn(self.cdims, self.lay.struct, self.q_act, self.act_rows, self.act_start,
                              self.n_act, pages, self.o_act[l], None, self.ws_attn)
 
+    def decode_attention(self, l: int, q, o, lse=None):
+        """Decode attention of each request's last token over layer l's mixed
+        cache (sx_decode_attn); q [n_req, Hq, d], o [n_req, Hq*d]."""
+        if not hasattr(self, "ws_dec"):
+            self.ws_dec = workspace(L.SX_OP_DECODE, self.cdims, self.n_tok, 0, self.n_req, self.device)
+        L.sx_decode_attn(self.cdims, self.lay.struct, q, self.req_pools[l].struct(), o, lse, self.ws_dec)
+
     def forward(self, timer=None, keep_full_outputs: bool = False):
         """One prefill pass of the batch through every layer."""
         for l in range(self.t):

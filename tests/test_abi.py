@@ -146,6 +146,22 @@ def test_plan_layout_matches_oracle_random_batches(overflow):
             off += T
 
 
+def test_decode_validation():
+    lib = L.lib()
+    lay = _layout()
+    pages = L.Pages(0x1000, 0x1000, 4)
+    d32 = _dims(dtype=L.SX_F32)
+    assert lib.sx_decode_attn(C.byref(d32), C.byref(lay), FAKE, C.byref(pages), FAKE, None, FAKE, 1 << 20,
+                              None) == L.SX_EUNSUPPORTED
+    d = _dims()
+    need = lib.sx_workspace_bytes(L.SX_OP_DECODE, C.byref(d), 16, 0, 1)
+    assert need > 0
+    assert lib.sx_decode_attn(C.byref(d), C.byref(lay), FAKE, C.byref(pages), FAKE, None, FAKE, need - 1,
+                              None) == L.SX_EWORKSPACE
+    assert lib.sx_decode_attn(C.byref(d), C.byref(lay), None, C.byref(pages), FAKE, None, FAKE, need,
+                              None) == L.SX_EINVAL
+
+
 def test_plan_layout_rejects_bad_ratio():
     with pytest.raises(L.SxError):
         L.sx_plan_layout([([(True, 10)], (3, 2))])
