@@ -16,6 +16,7 @@ t_layer = (sum over sparse layers of realign + recompute + sparse attention
 + the one selection) / 28, all from HIP events on the launch stream.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --sweep      (chat32k: time per pass vs threshold)
 """
 
 from __future__ import annotations
@@ -47,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--threshold", type=int, default=4)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the rag32k line: the chat32k workload at thresholds "
+                         "0/10/15/20%% of the layers, plus full recompute and ratio 0%%")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain elementwise copy (torch.neg) of this many MiB of fp32 "
                          "before the timed region, as the byte-counter reference for rocprofv3")
@@ -162,6 +166,66 @@ def cpu_baseline(dims, plan, n_sparse: int, T: int, reused: int, seed: int = 424
             "seconds_per_layer": layer_s, "parts_s": {k_: round(v, 4) for k_, v in t.items()}}
 
 
+def sweep(args):
+    """The chat workload (instruction | reused history | the history's last,
+    uncached partial block | question) through the full+sparse hybrid stack
+    at several thresholds t (the trade-off of §3.4 and Table 1): one prefill
+    pass of 32 layers, timed with HIP events, per configuration."""
+    import torch
+    from segment_level_kv_amd import synth
+    from segment_level_kv_amd.stack import HybridStackRun
+    dims = synth.LLAMA8B
+    seg_lengths, layout, p_src = synth.chat_layout()
+    seg_len = {i: n for i, n in enumerate(seg_lengths)}
+    seg_p = {i: p for i, p in enumerate(p_src)}
+    n_layers = args.layers
+    T = sum(seg_len[v] if k == "reuse" else v for k, v in layout)
+    n_cache = sum(seg_lengths)
+    ratio = (10, 100)
+    configs = [("full recompute", n_layers, ratio)]
+    for frac in (0.0, 0.10, 0.15, 0.20):
+        configs.append((f"t={int(frac * 100)}%", int(round(frac * n_layers)), ratio))
+    configs.append(("ratio 0%, t=0", 0, (0, 100)))
+    points = []
+    for name, t, rt in configs:
+        inputs = synth.TorchStackInputs(2005, dims, n_layers, T, n_cache, t, "cuda")
+        run = HybridStackRun(dims, n_layers, t, [layout], seg_len, seg_p, [rt], inputs, "cuda")
+        run.build_caches()
+        for _ in range(args.warmup):
+            run.forward()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(args.steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            run.forward()
+            b.record()
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        points.append({"config": name, "threshold_layers": t, "ratio": f"{rt[0]}%",
+                       "active_rows": int(run.n_act), "ms_per_pass": round(ms, 3),
+                       "prefill_tokens_per_s": round(T / (ms * 1e-3), 1)})
+        print(f"# {name}: {ms:.3f} ms", file=sys.stderr, flush=True)
+        del run, inputs
+        torch.cuda.empty_cache()
+    full_ms = points[0]["ms_per_pass"]
+    for p in points:
+        p["speedup_vs_full_recompute"] = round(full_ms / p["ms_per_pass"], 2)
+    out = {
+        "metric": "chat32k prefill time per 32-layer pass vs full+sparse threshold",
+        "unit": "ms", "higher_is_better": False, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": ("chat32k: 32-layer Llama-3-8B-shaped attention stack, "
+                                f"120-token instruction + {n_cache}-token reused history + "
+                                f"{T - 120 - n_cache - 80}-token uncached last block + 80-token "
+                                f"question = {T} tokens"), "tokens": T},
+        "points": points,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -172,6 +236,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.sweep:
+        sweep(args)
+        return
     from segment_level_kv_amd import synth
     from segment_level_kv_amd.stack import HybridStackRun, phase_counts, phase_ms
 

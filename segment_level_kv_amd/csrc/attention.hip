@@ -199,10 +199,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_work(
   for (int t0 = 0; t0 < n_tiles; t0 += kBuildThreads) {
     const int t = t0 + tid;
     int nc = 0;
-    if (t < n_tiles) {
-      const int last_start = (tiles[t].pmin / KB) * KB;
-      nc = split && last_start > 0 ? 1 + (last_start + chunk - 1) / chunk : 1;
-    }
+    if (t < n_tiles) nc = split ? (tiles[t].pmax + chunk) / chunk : 1;   // ceil((pmax+1)/chunk)
     int tot_i, tot_s, tot_m;
     const int io = item_base + build_scan(nc, sh_scan, &tot_i);
     const int so = slot_base + build_scan(nc > 1 ? nc : 0, sh_scan, &tot_s);
@@ -227,32 +224,21 @@ __global__ __launch_bounds__(kBuildThreads) void build_work(
   const int n_items = min(item_base, max_items);
 
   // ---- items, counting-sorted ------------------------------------------------------
-  // Chunks of a split tile sit on a grid shared by all tiles: full chunks
-  // [c*chunk, (c+1)*chunk) below the block holding pmin, then the remainder
-  // up to that block, then the last chunk from that block to pmax (so every
-  // row sees at least one key of every chunk).  Order: full chunks first,
-  // by chunk index (the workgroups running together on an XCD then stream
-  // the same keys of one kv head, which its L2 shares), then the other items
-  // longest first.
+  // Chunks of a split tile sit on a grid shared by all tiles: [c*chunk,
+  // (c+1)*chunk) up to pmax.  A chunk may lie wholly past some rows of the
+  // tile (rows far apart in position); those rows get an empty partial
+  // (m = -inf, l = 0) that the merge weighs with 0.  Order: full chunks
+  // first, by chunk index (the workgroups running together on an XCD then
+  // stream the same keys of one kv head, which its L2 shares), then the
+  // other items longest first.
   for (int i = tid; i < kFullKeys + kSortBuckets; i += kBuildThreads) hist[i] = 0;
   __syncthreads();
   auto chunk_range = [&](const TileInfo& T, int c, int& k0, int& k1) {
-    if (T.n_chunks == 1) {
-      k0 = 0;
-      k1 = T.pmax + 1;
-      return;
-    }
-    const int last_start = (T.pmin / KB) * KB;
-    if (c == T.n_chunks - 1) {
-      k0 = last_start;
-      k1 = T.pmax + 1;
-    } else {
-      k0 = c * chunk;
-      k1 = min(k0 + chunk, last_start);
-    }
+    k0 = c * chunk;
+    k1 = min(k0 + chunk, T.pmax + 1);
   };
   auto sort_key = [&](const TileInfo& T, int c, int k0, int k1) {
-    if (T.n_chunks > 1 && c < T.n_chunks - 1 && k1 - k0 == chunk) return min(c, kFullKeys - 1);
+    if (T.n_chunks > 1 && k1 - k0 == chunk) return min(c, kFullKeys - 1);
     return kFullKeys + kSortBuckets - 1 - min((k1 - k0 - 1) / KB, kSortBuckets - 1);
   };
   for (int t = tid; t < n_tiles; t += kBuildThreads) {
@@ -558,9 +544,14 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
     const float mx = half_max(fmaxf(u0, u1));
     const bool any = __ballot((mx - m_run[nb]) * c > 8.f) != 0ull;
     const float m_new = any ? fmaxf(m_run[nb], mx) : m_run[nb];
-    alpha[nb] = __builtin_amdgcn_exp2f((m_run[nb] - m_new) * c);
+    // A key chunk of a split tile can lie wholly past a row's position: the
+    // row then has no key yet, m stays -inf, and the exponent reference is 0
+    // (p = 0, alpha = 0) instead of -inf - -inf.  Only masked steps can see
+    // such a row.
+    const float m_ref = (mask && m_new == -INFINITY) ? 0.f : m_new;
+    alpha[nb] = __builtin_amdgcn_exp2f((m_run[nb] - m_ref) * c);
     m_run[nb] = m_new;
-    const float mc = m_new * c;
+    const float mc = m_ref * c;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float p[8];
@@ -766,7 +757,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
         part_ml[2 * pslot + 1] = l_tot;
       }
       if (WITH_O) {                        // normalised partial output, fp16
-        const float inv = 1.f / l_tot;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // a chunk past the row: o = 0
         uint16_t* op = part_o + pslot * 128 + 4 * hl;
 #pragma unroll
         for (int md = 0; md < 4; ++md)

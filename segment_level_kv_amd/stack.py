@@ -196,6 +196,8 @@ class HybridStackRun:
             self.full_layer(l, timer)
             if keep_full_outputs:
                 self.o_full_layers.append(self.o_full.clone())
+        if self.t >= self.n_layers:   # every layer full: nothing to select for
+            return
         if self.t > 0:
             self.select(self.t - 1, timer)
             for l in range(self.t, self.n_layers):

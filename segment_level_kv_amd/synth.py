@@ -291,6 +291,23 @@ def agent_case(seed: int = 1004, n_req: int = 4, target: int = 65536, n_pool: in
     return make_case("agent64k", LLAMA8B, lengths, layouts, ratios, seed + 17, p_src_max=8192)
 
 
+def chat_layout(instruction: int = 120, history: int = 31000, question: int = 80,
+                block: int = 16):
+    """Multi-round chat prompt: a fixed instruction prefix, the reused
+    conversation history and the question (Appendix B.1 prompt shape).
+
+    The history was cached alone, from position 0, by an earlier request;
+    only its whole blocks were cached (the final, incomplete block is not),
+    so its last history % block tokens are recomputed with the new text.
+    Returns (seg_lengths, layout, p_src)."""
+    cached = (history // block) * block
+    layout = [("new", instruction), ("reuse", 0)]
+    if history > cached:
+        layout.append(("new", history - cached))
+    layout.append(("new", question))
+    return [cached], layout, [0]
+
+
 def qwen_layout(n_seg: int = 32, seg_len: int = 4000, suffix: int = 1024):
     seg_lengths = [seg_len] * n_seg
     layout = [("reuse", i) for i in range(n_seg)] + [("new", suffix)]

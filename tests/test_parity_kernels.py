@@ -360,6 +360,60 @@ def test_topk_bit_exact_adversarial():
         off += ks[r]
 
 
+def test_sparse_attention_rows_far_apart():
+    """A handful of active rows at the start and at the end of a long
+    request share query tiles: the tiles are split on the key grid, and for
+    the early rows most chunks lie wholly past their position (empty
+    partials that the merge must weigh with 0).  The LSE-only probe pass is
+    checked on the same rows."""
+    dims = SHAPES["llama"]
+    lens = [20000, 700]
+    say(f"[attn far apart] lens={lens}")
+    rng, seq, pool, kh, vh, bt = _attn_inputs(dims, lens, 91)
+    sel0 = np.r_[0:40, 19960:20000]
+    sel1 = np.r_[3:9, 690:700]
+    rows = np.concatenate([sel0 + seq[0], sel1 + seq[1]]).astype(np.int32)
+    starts = [0, len(sel0), len(sel0) + len(sel1)]
+    n_rows = len(rows)
+    q = _store(rng.standard_normal((n_rows, dims.n_q_heads, dims.head_dim)) * 2.0, dims)
+    dt = LY.storage_dtype(dims.dtype)
+    lay = LY.DeviceLayout(seq, bt, LY.rope_table(dims.theta, dims.head_dim, 16, DEV), DEV)
+    cd = LY.make_dims(dims)
+    qd = torch.from_numpy(q).to(dt).to(DEV)
+    rd = torch.from_numpy(rows).to(DEV)
+    sd = torch.from_numpy(np.array(starts, np.int32)).to(DEV)
+    o = torch.zeros((n_rows, dims.n_q_heads * dims.head_dim), dtype=dt, device=DEV)
+    lse = torch.zeros((n_rows, dims.n_q_heads), dtype=torch.float32, device=DEV)
+    ws = LY.workspace(L.SX_OP_SPARSE_ATTN, cd, int(seq[-1]), n_rows, len(lens), DEV)
+    L.sx_sparse_attn(cd, lay.struct, qd, rd, sd, n_rows, pool.struct(), o, lse, ws)
+    # the selection's internal probe: LSE only (Sparse-Q rows = these rows)
+    n_tok = int(seq[-1])
+    tok_class = torch.zeros(n_tok, dtype=torch.uint8, device=DEV)
+    tok_class[rd.long()] = 1
+    k_sel = torch.zeros(len(lens), dtype=torch.int32, device=DEV)
+    sel_rows = torch.empty(1, dtype=torch.int32, device=DEV)
+    scores = torch.empty(n_tok, dtype=torch.float32, device=DEV)
+    ws2 = LY.workspace(L.SX_OP_SELECT, cd, n_tok, n_rows, len(lens), DEV)
+    L.sx_select_topk(cd, lay.struct, qd, None, rd, sd, n_rows, None, pool.struct(), tok_class, k_sel,
+                     sel_rows, None, scores, ws2)
+    torch.cuda.synchronize()
+    og = o.float().cpu().double().numpy()
+    lg = lse.cpu().double().numpy()
+    sg = scores.cpu().double().numpy()
+    for r in range(len(lens)):
+        K, V = _logical(kh, vh, bt[r], 0, lens[r])
+        sl = slice(starts[r], starts[r + 1])
+        pos = rows[sl] - seq[r]
+        ref, lref = oracle.causal_attention(q[sl], pos, K, V)
+        assert_close_bf16(og[sl], ref.reshape(len(ref), -1), what=f"O req {r}")
+        assert np.max(np.abs(lg[sl] - lref)) < 2e-3
+        # mass scores over this request's tokens: each row and head gives mass 1 in total
+        s_ref = oracle.attention_mass_scores(q[sl], pos, K, lref)
+        s_got = sg[seq[r]:seq[r + 1]]
+        assert np.all(np.abs(s_got - s_ref) <= 2e-3 * s_ref + 1e-4 * s_ref.max())
+        assert abs(s_got.sum() - len(pos) * dims.n_q_heads) < 1e-2 * len(pos) * dims.n_q_heads
+
+
 @pytest.mark.parametrize("shape", ["llama", "qwen"])
 def test_sparse_attention_many_chunks_and_nan_tail(shape):
     """Long requests with few active rows: every query tile is split into
