@@ -40,8 +40,13 @@ struct Gemm2Smem {
     Gemm2Stage st[NST2];
     float c[BM2][LDC];
   };
-  int32_t row_req[BM2];
-  int32_t row_idx[BM2];
+  // per output row, resolved once per tile: page of the token (-1 if the row
+  // or its page is invalid; for Q heads only row_ok matters), its slot and
+  // its RoPE position
+  int32_t row_page[BM2];
+  int32_t row_slot[BM2];
+  int32_t row_pos[BM2];
+  int32_t row_ok[BM2];
 };
 
 __global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
@@ -76,8 +81,10 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
       r = find_request(lay.seq_start, lay.n_req, tok);
       if (r >= 0) idx = tok - lay.seq_start[r];
     }
-    sm.row_req[tid] = r;
-    sm.row_idx[tid] = idx;
+    sm.row_ok[tid] = r >= 0;
+    sm.row_page[tid] = r >= 0 ? page_of(lay, n_pages, r, idx) : -1;
+    sm.row_slot[tid] = idx & (kPage - 1);
+    sm.row_pos[tid] = r >= 0 ? rope_pos(lay, r, idx) : 0;
   }
 
   // ---- copy plan: lane L of copy i moves one 16-byte chunk --------------
@@ -182,29 +189,36 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
   __syncthreads();
 
   if (head < hq + hkv) {
-    // Q or K head: rotate-half pairs (e, e+64), 8 pairs per unit.
+    // Q or K head: rotate-half pairs (e, e+64), 8 pairs per unit; a thread
+    // takes 8 units (rows tid/8 + 32 k), first loading all their RoPE table
+    // entries, then rotating and storing.
     const bool is_q = head < hq;
     const int g = head - hq;
-    for (int u = tid; u < BM2 * 8; u += 256) {
-      const int m = u >> 3, c = u & 7;
-      const int r = sm.row_req[m];
-      if (r < 0) continue;
-      const int idx = sm.row_idx[m];
-      uint16_t* dst;
+    constexpr int kUnits = BM2 * 8 / 256;
+    const int c = tid & 7;
+    f32x4 tabv[kUnits][4];
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) {
+      const int m = (tid >> 3) + 32 * k;
+      const f32x4* tab = reinterpret_cast<const f32x4*>(lay.rope_tab + (size_t)sm.row_pos[m] * 128 + c * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tabv[k][i] = tab[i];
+    }
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) {
+      const int m = (tid >> 3) + 32 * k;
+      uint16_t* dst = nullptr;
       if (is_q) {
-        if (!q_out) continue;
-        dst = q_out + ((size_t)(m0 + m) * hq + head) * 128;
+        if (q_out && sm.row_ok[m]) dst = q_out + ((size_t)(m0 + m) * hq + head) * 128;
       } else {
-        const int page = page_of(lay, n_pages, r, idx);
-        if (page < 0) continue;
-        dst = kpool + (((size_t)page * hkv + g) * kPage + (idx & (kPage - 1))) * 128;
+        const int page = sm.row_page[m];
+        if (page >= 0) dst = kpool + (((size_t)page * hkv + g) * kPage + sm.row_slot[m]) * 128;
       }
-      const float* tab = lay.rope_tab + (size_t)rope_pos(lay, r, idx) * 128 + c * 16;
       float olo[8], ohi[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float lo = sm.c[m][c * 8 + e], hi = sm.c[m][64 + c * 8 + e];
-        const float cs = tab[2 * e], sn = tab[2 * e + 1];
+        const float cs = tabv[k][e >> 1][2 * (e & 1)], sn = tabv[k][e >> 1][2 * (e & 1) + 1];
         olo[e] = lo * cs - hi * sn;
         ohi[e] = lo * sn + hi * cs;
       }
@@ -214,20 +228,24 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
         plo[e] = pack_bf2(olo[2 * e], olo[2 * e + 1]);
         phi[e] = pack_bf2(ohi[2 * e], ohi[2 * e + 1]);
       }
-      *reinterpret_cast<u32x4*>(dst + c * 8) = plo;
-      *reinterpret_cast<u32x4*>(dst + 64 + c * 8) = phi;
+      if (dst) {
+        *reinterpret_cast<u32x4*>(dst + c * 8) = plo;
+        *reinterpret_cast<u32x4*>(dst + 64 + c * 8) = phi;
+      }
     }
   } else {
-    // V head: page layout [d][slot]; consecutive lanes take consecutive rows.
+    // V head: page layout [d][slot]; thread tid takes output row tid (all
+    // 128 d of one token, 2-byte stores 32 bytes apart in its page).
     const int g = head - hq - hkv;
-    for (int u = tid; u < BM2 * 128; u += 256) {
-      const int m = u & (BM2 - 1), e = u >> 8;
-      const int r = sm.row_req[m];
-      if (r < 0) continue;
-      const int idx = sm.row_idx[m];
-      const int page = page_of(lay, n_pages, r, idx);
-      if (page < 0) continue;
-      vpool[(((size_t)page * hkv + g) * 128 + e) * kPage + (idx & (kPage - 1))] = f2bf(sm.c[m][e]);
+    const int page = sm.row_page[tid];
+    if (page >= 0) {
+      uint16_t* base = vpool + ((size_t)page * hkv + g) * 128 * kPage + sm.row_slot[tid];
+#pragma unroll 4
+      for (int e = 0; e < 128; e += 4) {
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(&sm.c[tid][e]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) base[(e + i) * kPage] = f2bf(c4[i]);
+      }
     }
   }
 }
