@@ -118,7 +118,11 @@ class HybridStackRun:
         self.q_full = torch.empty((self.n_tok, hq, d), dtype=self.dt, device=device)
         self.o_full = torch.empty((self.n_tok, hq * d), dtype=self.dt, device=device)
         self.lse_full = torch.empty((self.n_tok, hq), dtype=torch.float32, device=device)
-        self.q_act = torch.empty((max(self.n_act, 1), hq, d), dtype=self.dt, device=device)
+        # two Q buffers of the active rows: with layers pipelined, layer l+1's
+        # recompute writes one while layer l's attention reads the other
+        self.q_act_buf = [torch.empty((max(self.n_act, 1), hq, d), dtype=self.dt, device=device)
+                          for _ in range(2)]
+        self.q_act = self.q_act_buf[0]
         self.o_act = [torch.empty((max(self.n_act, 1), hq * d), dtype=self.dt, device=device)
                       for _ in range(n_layers)]
         self.sel_rows = torch.empty(max(self.n_sel, 1), dtype=torch.int32, device=device)
@@ -170,7 +174,8 @@ class HybridStackRun:
                              self.n_sq, None, pages, self.tok_class, self.k_sel, self.sel_rows,
                              self.act_rows, self.scores, self.ws_sel)
 
-    def sparse_layer(self, l: int, timer=None, realign: bool = True):
+    def sparse_prep(self, l: int, timer=None, realign: bool = True):
+        """Layer l's cache and queries: realign its reused runs, recompute A."""
         x, w, _ = self.inputs(l)
         pages = self.req_pools[l].struct()
         if realign:
@@ -178,10 +183,54 @@ class HybridStackRun:
                 L.sx_rope_realign(self.cdims, self.lay.struct, self.src_pools[l].struct(), pages, self.jobs,
                                   len(self.jobs_h))
         with _phase(timer, "recompute"):
-            L.sx_recompute_kv(self.cdims, self.lay.struct, x, self.act_rows, self.n_act, w, pages, self.q_act)
+            L.sx_recompute_kv(self.cdims, self.lay.struct, x, self.act_rows, self.n_act, w, pages,
+                              self.q_act_buf[l % 2])
+
+    def sparse_attn(self, l: int, timer=None):
         with _phase(timer, "sparse_attn"):
-            L.sx_sparse_attn(self.cdims, self.lay.struct, self.q_act, self.act_rows, self.act_start,
-                             self.n_act, pages, self.o_act[l], None, self.ws_attn)
+            L.sx_sparse_attn(self.cdims, self.lay.struct, self.q_act_buf[l % 2], self.act_rows,
+                             self.act_start, self.n_act, self.req_pools[l].struct(), self.o_act[l], None,
+                             self.ws_attn)
+
+    def sparse_layer(self, l: int, timer=None, realign: bool = True):
+        self.sparse_prep(l, timer, realign)
+        self.sparse_attn(l, timer)
+
+    def sparse_layers_pipelined(self, first: int, timer=None, first_realigned: bool = False):
+        """Sparse layers first..n-1 on two streams: layer l+1's realign and
+        recompute (side stream) run while layer l's attention (launch
+        stream) does; events order each attention after its own layer's
+        preparation and each preparation after the attention that last read
+        its Q buffer.  The launch stream ends after the last attention."""
+        import torch
+        main = torch.cuda.current_stream()
+        if not hasattr(self, "side_stream"):
+            self.side_stream = torch.cuda.Stream()   # default priority
+        side = self.side_stream
+        start = torch.cuda.Event()
+        start.record(main)
+        side.wait_event(start)
+        prep_done, attn_done = {}, {}
+
+        def prep(l):
+            if l - 2 >= first:
+                side.wait_event(attn_done[l - 2])
+            with torch.cuda.stream(side):
+                self.sparse_prep(l, timer, realign=not (first_realigned and l == first))
+                ev = torch.cuda.Event()
+                ev.record(side)
+            prep_done[l] = ev
+
+        prep(first)
+        for l in range(first, self.n_layers):
+            if l + 1 < self.n_layers:
+                prep(l + 1)
+            main.wait_event(prep_done[l])
+            self.sparse_attn(l, timer)
+            ev = torch.cuda.Event()
+            ev.record(main)
+            attn_done[l] = ev
+        # the side stream's last work is done before the last attention began
 
     def decode_attention(self, l: int, q, o, lse=None):
         """Decode attention of each request's last token over layer l's mixed
@@ -190,23 +239,46 @@ class HybridStackRun:
             self.ws_dec = workspace(L.SX_OP_DECODE, self.cdims, self.n_tok, 0, self.n_req, self.device)
         L.sx_decode_attn(self.cdims, self.lay.struct, q, self.req_pools[l].struct(), o, lse, self.ws_dec)
 
-    def forward(self, timer=None, keep_full_outputs: bool = False):
-        """One prefill pass of the batch through every layer."""
+    def forward(self, timer=None, keep_full_outputs: bool = False, pipelined: bool = False,
+                marks=None):
+        """One prefill pass of the batch through every layer (pipelined: the
+        sparse layers on two streams, see sparse_layers_pipelined).  marks
+        (a dict, optional) receives events on the launch stream: "sparse"
+        just before the selection, "end" after the last layer."""
+        import torch
+
+        def mark(name):
+            if marks is not None:
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record()
+                marks[name] = ev
+
+        self._forward(timer, keep_full_outputs, pipelined, mark)
+        mark("end")
+
+    def _forward(self, timer, keep_full_outputs, pipelined, mark):
         for l in range(self.t):
             self.full_layer(l, timer)
             if keep_full_outputs:
                 self.o_full_layers.append(self.o_full.clone())
         if self.t >= self.n_layers:   # every layer full: nothing to select for
             return
+        mark("sparse")
         if self.t > 0:
             self.select(self.t - 1, timer)
-            for l in range(self.t, self.n_layers):
-                self.sparse_layer(l, timer)
+            if pipelined:
+                self.sparse_layers_pipelined(self.t, timer)
+            else:
+                for l in range(self.t, self.n_layers):
+                    self.sparse_layer(l, timer)
         else:
             self.select_in_layer(0, timer)
-            self.sparse_layer(0, timer, realign=False)
-            for l in range(1, self.n_layers):
-                self.sparse_layer(l, timer)
+            if pipelined:
+                self.sparse_layers_pipelined(0, timer, first_realigned=True)
+            else:
+                self.sparse_layer(0, timer, realign=False)
+                for l in range(1, self.n_layers):
+                    self.sparse_layer(l, timer)
 
 
 class _NoPhase:

@@ -64,16 +64,18 @@ def _segments(xc, wq, wk, wv, d):
     return out
 
 
-@pytest.mark.parametrize("t", [0, 1, 2])
-def test_hybrid_stack_parity(t):
+@pytest.mark.parametrize("t,pipelined", [(0, False), (1, False), (2, False), (0, True), (1, True)])
+def test_hybrid_stack_parity(t, pipelined):
+    """pipelined: the sparse layers on two streams (layer l+1's realign and
+    recompute while layer l attends); the results must not change."""
     d = SMALL
-    say(f"[stack] layers={N_LAYERS} threshold={t}")
+    say(f"[stack] layers={N_LAYERS} threshold={t} pipelined={pipelined}")
     n_tok = sum(SEG_LEN[v] if k == "reuse" else v for k, v in LAYOUT)
     n_cache = sum(SEG_LEN.values())
     inputs = synth.TorchStackInputs(77 + t, d, N_LAYERS, n_tok, n_cache, t, DEV)
     run = HybridStackRun(d, N_LAYERS, t, [LAYOUT], SEG_LEN, SEG_P, [RATIO], inputs, DEV)
     run.build_caches()
-    run.forward(keep_full_outputs=True)
+    run.forward(keep_full_outputs=True, pipelined=pipelined)
     torch.cuda.synchronize()
 
     pieces = [(k, SEG_LEN[v] if k == "reuse" else v) for k, v in LAYOUT]
