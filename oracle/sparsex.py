@@ -337,7 +337,7 @@ def _positions(T: int, pos0: int) -> np.ndarray:
 
 def sparse_layer(x, wq, wk, wv, plan: dict, segments, theta: float, n_q_heads: int,
                  n_kv_heads: int, head_dim: int, dtype: str, selected=None, lse_probe=None,
-                 q_probe=None, k_probe=None, pos0: int = 0) -> dict:
+                 q_probe=None, k_probe=None, pos0: int = 0, out_rows=None) -> dict:
     """One SparseX prefill layer of one request.
 
     x [T, hidden]: layer input (storage values).  plan: from plan_request.
@@ -360,8 +360,14 @@ def sparse_layer(x, wq, wk, wv, plan: dict, segments, theta: float, n_q_heads: i
     the k/v of S replace the realigned ones; the probe of step 3 uses the
     mixed cache of this layer.
 
+    out_rows (for checks at full size): None computes O for every row of A;
+    an int n computes it only for n rows of A spread evenly over it (first
+    and last included); an array gives the rows (a subset of A).  O,
+    O_exact and lse_A then hold those rows, listed in "O_rows".
+
     Returns dict with O [|A|, Hq*d] (rounded), O_exact (unrounded), A, S,
-    scores (None if not probed), lse_sq, K, V (final mixed cache), q_A.
+    scores (None if not probed), lse_sq, K, V (final mixed cache), q_A,
+    O_rows.
     """
     T = plan["T"]
     pos = _positions(T, pos0)
@@ -399,10 +405,18 @@ def sparse_layer(x, wq, wk, wv, plan: dict, segments, theta: float, n_q_heads: i
     q_A = np.empty((len(A), n_q_heads, head_dim))
     q_A[np.searchsorted(A, sq)] = q_sq
     q_A[np.searchsorted(A, S)] = q_S
-    O, lse_A = causal_attention(q_A, A, K, V)
-    O = O.reshape(len(A), n_q_heads * head_dim)
+    if out_rows is None:
+        rows = A
+    elif np.isscalar(out_rows):
+        rows = A[np.unique(np.linspace(0, len(A) - 1, int(out_rows)).round().astype(np.int64))]
+    else:
+        rows = np.asarray(out_rows, dtype=np.int64)
+        if not np.isin(rows, A).all():
+            raise ValueError("out_rows must be active rows")
+    O, lse_A = causal_attention(q_A[np.searchsorted(A, rows)], rows, K, V)
+    O = O.reshape(len(rows), n_q_heads * head_dim)
     return dict(O=round_store(O, dtype), O_exact=O, A=A, S=S, scores=scores, lse_sq=lse_sq,
-                lse_A=lse_A, K=K, V=V, q_A=q_A, q_sq=q_sq)
+                lse_A=lse_A, K=K, V=V, q_A=q_A, q_sq=q_sq, O_rows=rows)
 
 
 def full_layer(x, wq, wk, wv, theta: float, n_q_heads: int, n_kv_heads: int, head_dim: int,

@@ -219,3 +219,19 @@ def test_overflow_covering_every_reused_piece_is_full_prefill(dims):
     assert len(out["A"]) == plan["T"] and plan["k"] == 0
     ref = _straight_full_prefill(case)
     assert np.max(np.abs(out["O_exact"] - ref)) < 1e-9
+
+
+def test_sampled_output_rows_equal_the_full_computation():
+    """out_rows only restricts which rows of A get an output: the same rows
+    of the full computation, bit for bit."""
+    case = _case(SMALL_F32, LAYOUT, LENS, noise=0.5)
+    plan, full = _run(case, (1, 3))
+    _, part = _run(case, (1, 3), out_rows=5)
+    rows = part["O_rows"]
+    assert len(rows) == 5 and rows[0] == full["A"][0] and rows[-1] == full["A"][-1]
+    idx = np.searchsorted(full["A"], rows)
+    assert np.array_equal(part["O_exact"], full["O_exact"][idx])
+    _, given = _run(case, (1, 3), out_rows=full["A"][[1, 3]])
+    assert np.array_equal(given["O_exact"], full["O_exact"][[1, 3]])
+    with pytest.raises(ValueError):
+        _run(case, (1, 3), out_rows=[int(np.setdiff1d(np.arange(plan["T"]), full["A"])[0])])
