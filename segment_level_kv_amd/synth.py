@@ -314,6 +314,15 @@ def qwen_layout(n_seg: int = 32, seg_len: int = 4000, suffix: int = 1024):
     return seg_lengths, layout
 
 
+def qwen128k_case(seed: int = 1005, ratio=(10, 100)) -> LayerCase:
+    """One sparse layer of the long-context mix on Qwen2.5-7B shapes: 32
+    reused segments of 4,000 tokens, each cached alone at an offset in
+    [0, 128K - 4000], then a 1,024-token new suffix (129,024 tokens)."""
+    seg_lengths, layout = qwen_layout()
+    return make_case("qwen128k", QWEN7B, seg_lengths, [layout], [ratio], seed,
+                     p_src_max=128 * 1024)
+
+
 def page_permutation(seed: int, n_pages: int) -> np.ndarray:
     """Seeded shuffle of physical page ids (so block tables are not
     contiguous)."""

@@ -39,6 +39,30 @@ def assert_close_bf16(got, ref, atol=1e-2, rel=BF16_HALF_STEP_REL, what=""):
     return float(err.max())
 
 
+def assert_close_bf16_rotated(got, ref, atol=1e-2, what=""):
+    """Keys [..., d] that went through two bf16 stores with a RoPE rotation
+    between them (the segment cache, then the realigned copy).
+
+    The rotation mixes the two halves of each pair (e, e + d/2): a one-step
+    difference in the first store of one component reaches the other
+    component scaled by the sine, so the bound is relative to the pair's
+    norm n_e (unchanged by the rotation): |g - r| <= atol + 2^-7 sqrt(2) n_e
+    (first store) + 2^-8 |r| (second store)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    h = ref.shape[-1] // 2
+    norm = np.sqrt(ref[..., :h] ** 2 + ref[..., h:] ** 2)
+    norm = np.concatenate([norm, norm], axis=-1)
+    tol = atol + BF16_STEP_REL * np.sqrt(2.0) * norm + BF16_HALF_STEP_REL * np.abs(ref)
+    err = np.abs(got - ref)
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; "
+                           f"max err {err.max():.3g} at {np.unravel_index(err.argmax(), err.shape)}")
+    return float(err.max())
+
+
 def assert_close_f32(got, ref, rel=1e-4, what=""):
     """fp32 storage: max |g - r| <= rel * max |r| per tensor."""
     got = np.asarray(got, dtype=np.float64)
