@@ -250,6 +250,124 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
   }
 }
 
+// bf16 path for a few rows (at most 64: a decode step's new tokens, a small
+// Sparse-Q set): reading W dominates, so the work is spread over columns
+// and the reduction dimension instead of row tiles.  Workgroup (head,
+// quarter q) owns the 16 rotate-half pairs (16q + j, 64 + 16q + j) of one
+// head, i.e. 32 output columns: RoPE pairs stay inside the workgroup.  Its
+// 8 waves take interleaved 32-wide k-steps (v_mfma_f32_16x16x32_bf16: A =
+// x rows, B = the 32 W rows), each with the operands of 8 k-steps in flight,
+// and are summed in LDS in wave order.  RB row blocks of 16 share each W
+// fragment.
+constexpr int kSkWaves = 8, kSkThreads = 64 * kSkWaves;
+template <int RB>
+__global__ __launch_bounds__(kSkThreads) void qkv_skinny_bf16(
+    const uint16_t* __restrict__ x, int hidden, const int32_t* __restrict__ rows, int n_rows,
+    const uint16_t* __restrict__ w, int head0, sx_layout lay, int n_pages,
+    uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool, uint16_t* __restrict__ q_out,
+    int hq, int hkv) {
+  constexpr int NR = 16 * RB;
+  __shared__ float red[kSkWaves][NR][33];
+  __shared__ int32_t s_tok[NR], s_ok[NR], s_page[NR], s_slot[NR], s_pos[NR];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int head = head0 + blockIdx.x / 4, qd = blockIdx.x % 4;
+  if (tid < NR) {
+    int tok = tid < n_rows ? rows[tid] : -1;
+    const int r = tok >= 0 ? find_request(lay.seq_start, lay.n_req, tok) : -1;
+    const int idx = r >= 0 ? tok - lay.seq_start[r] : 0;
+    s_ok[tid] = r >= 0;
+    s_tok[tid] = (tok >= 0 && tok < lay.n_tok) ? tok : 0;   // rows past n_rows read token 0
+    s_page[tid] = r >= 0 ? page_of(lay, n_pages, r, idx) : -1;
+    s_slot[tid] = idx & (kPage - 1);
+    s_pos[tid] = r >= 0 ? rope_pos(lay, r, idx) : 0;
+  }
+  __syncthreads();
+  const int lr = lane & 15, lq = lane >> 4;
+  // this lane's A rows (one per row block) and B rows (one per column block)
+  const uint16_t* xa[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) xa[rb] = x + (size_t)s_tok[16 * rb + lr] * hidden + 8 * lq;
+  const uint16_t* wb[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+    wb[cb] = w + ((size_t)head * 128 + 64 * cb + 16 * qd + lr) * hidden + 8 * lq;
+  f32x4 acc[RB][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int n_ks = hidden / 32;
+  constexpr int U = 8;                       // k-steps whose operands are loaded together
+  int ks = wave;
+  for (; ks + kSkWaves * (U - 1) < n_ks; ks += kSkWaves * U) {
+    bf16x8 a[U][RB], b[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (ks + kSkWaves * u) * 32;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) a[u][rb] = *reinterpret_cast<const bf16x8*>(xa[rb] + k);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) b[u][cb] = *reinterpret_cast<const bf16x8*>(wb[cb] + k);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][rb], b[u][cb], acc[rb][cb], 0, 0, 0);
+  }
+  for (; ks < n_ks; ks += kSkWaves) {
+    const int k = ks * 32;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            *reinterpret_cast<const bf16x8*>(xa[rb] + k), *reinterpret_cast<const bf16x8*>(wb[cb] + k),
+            acc[rb][cb], 0, 0, 0);
+  }
+  // D: row 4*lq + v of the row block, column lr of the column block
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave][16 * rb + 4 * lq + v][16 * cb + lr] = acc[rb][cb][v];
+  __syncthreads();
+  // one rotate-half pair (row m, e = 16 qd + j) per thread and step
+  for (int u = tid; u < NR * 16; u += kSkThreads) {
+    const int m = u >> 4, j = u & 15;
+    if (m >= n_rows || !s_ok[m]) continue;
+    float lo = 0.f, hi = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kSkWaves; ++ww) {
+      lo += red[ww][m][j];
+      hi += red[ww][m][16 + j];
+    }
+    const int e = 16 * qd + j;
+    if (head < hq + hkv) {
+      const float* tab = lay.rope_tab + (size_t)s_pos[m] * 128 + 2 * e;
+      const float cs = tab[0], sn = tab[1];
+      const float olo = lo * cs - hi * sn, ohi = lo * sn + hi * cs;
+      uint16_t* dst = nullptr;
+      if (head < hq) {
+        if (q_out) dst = q_out + ((size_t)m * hq + head) * 128;
+      } else if (s_page[m] >= 0) {
+        dst = kpool + (((size_t)s_page[m] * hkv + (head - hq)) * kPage + s_slot[m]) * 128;
+      }
+      if (dst) {
+        dst[e] = f2bf(olo);
+        dst[64 + e] = f2bf(ohi);
+      }
+    } else if (s_page[m] >= 0) {
+      uint16_t* dst = vpool + ((size_t)s_page[m] * hkv + (head - hq - hkv)) * 128 * kPage + s_slot[m];
+      dst[e * kPage] = f2bf(lo);
+      dst[(64 + e) * kPage] = f2bf(hi);
+    }
+  }
+}
+
 // fp32 storage: one workgroup per (row, head), one lane per rotate-half pair
 // (or per element for V); dot products accumulate in index order.
 template <int D>
@@ -310,7 +428,18 @@ sx_status launch_recompute(const sx_dims& dims, const sx_layout& lay, const void
   const int hq = dims.n_q_heads, hkv = dims.n_kv_heads;
   const int head0 = q_out ? 0 : hq;
   const int n_heads = hq + 2 * hkv - head0;
-  if (dims.dtype == SX_BF16) {
+  if (dims.dtype == SX_BF16 && n_rows <= 64) {
+    const dim3 grid(n_heads * 4);
+    auto go = [&](auto kernel) {
+      kernel<<<grid, kSkThreads, 0, stream>>>(
+          (const uint16_t*)x, dims.hidden, rows, n_rows, (const uint16_t*)w_qkv, head0, lay, kv.n_pages,
+          (uint16_t*)kv.k, (uint16_t*)kv.v, (uint16_t*)q_out, hq, hkv);
+    };
+    if (n_rows <= 16) go(qkv_skinny_bf16<1>);
+    else if (n_rows <= 32) go(qkv_skinny_bf16<2>);
+    else if (n_rows <= 48) go(qkv_skinny_bf16<3>);
+    else go(qkv_skinny_bf16<4>);
+  } else if (dims.dtype == SX_BF16) {
     const int mt = (n_rows + BM2 - 1) / BM2;
     const int total = mt * n_heads;
     const int grid = ((total + 7) / 8) * 8;

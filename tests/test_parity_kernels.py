@@ -120,7 +120,9 @@ def test_realign_parity_and_copy_semantics(shape):
 
 # ---------------------------------------------------------------- recompute --
 
-@pytest.mark.parametrize("shape,n_rows", [("llama", 300), ("qwen", 130), ("tiny", 40)])
+@pytest.mark.parametrize("shape,n_rows", [("llama", 300), ("qwen", 130), ("tiny", 40), ("llama", 1),
+                                          ("llama", 16), ("llama", 17), ("qwen", 32), ("llama", 48),
+                                          ("qwen", 64), ("llama", 65)])
 def test_recompute_parity_and_scatter(shape, n_rows):
     dims = SHAPES[shape]
     say(f"[recompute] shape={shape} rows={n_rows}")
