@@ -27,10 +27,17 @@ constexpr int GROUP_M = 4;
 // go global -> LDS directly (global_load_lds_dwordx4) into a ring of three
 // stages; each 128-byte LDS row keeps its 16-byte chunk c at position
 // c ^ (row & 7), so the 32 rows an MFMA operand read touches spread over
-// all banks.  Four waves, each 128 rows x 64 columns = 4 x 2 MFMA tiles of
-// 32 x 32 (acc in AGPRs); the operands of k-slice ks+1 are read from LDS
-// while the MFMAs of slice ks run.
+// all banks.  Eight waves, two per SIMD, each 64 rows x 64 columns = 2 x 2
+// MFMA tiles of 32 x 32 (one wave's barrier and LDS waits overlap the other's
+// MFMAs; four waves of 128 x 64 were 7% slower); the operands of k-slice ks+1
+// are read from LDS while the MFMAs of slice ks run.
 constexpr int BM2 = 256, NST2 = 3;
+constexpr int GW = 8;                  // waves per workgroup: two per SIMD
+constexpr int GT = 64 * GW;            // threads per workgroup
+constexpr int WROWS = BM2 / (GW / 2);  // output rows per wave (waves are (GW/2) x 2)
+constexpr int MI = WROWS / 32;         // 32 x 32 MFMA tiles per wave along M
+constexpr int NCA = BM2 * BK * 2 / 1024 / GW;   // 1 KB stage copies per wave: A
+constexpr int NCB = BN * BK * 2 / 1024 / GW;    //                              B
 struct Gemm2Stage {
   uint16_t a[BM2][BK];
   uint16_t b[BN][BK];
@@ -49,7 +56,7 @@ struct Gemm2Smem {
   int32_t row_ok[BM2];
 };
 
-__global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
+__global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
     const uint16_t* __restrict__ x, int hidden, const int32_t* __restrict__ rows, int n_rows,
     const uint16_t* __restrict__ w, int head0, int n_tiles_m, int n_tiles_n, sx_layout lay,
     int n_pages, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
@@ -74,7 +81,7 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
   const int head = head0 + nt;                 // 0..hq-1: Q, then K heads, then V heads
   const uint16_t* wt = w + (size_t)head * 128 * hidden;
 
-  {
+  if (tid < BM2) {
     int r = -1, idx = 0;
     if (m0 + tid < n_rows) {
       const int tok = rows[m0 + tid];
@@ -95,19 +102,19 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
   // never stored.
   typedef __attribute__((address_space(1))) const void* gptr_t;
   typedef __attribute__((address_space(3))) void* lptr_t;
-  size_t a_off[8];                           // byte offsets of this lane's chunks at k = 0
-  uint32_t b_off[4];
+  size_t a_off[NCA];                         // byte offsets of this lane's chunks at k = 0
+  uint32_t b_off[NCB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int R = 64 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < NCA; ++i) {
+    const int R = 8 * NCA * wave + 8 * i + (lane >> 3);
     const int m = m0 + R;
     int tok = m < n_rows ? rows[m] : 0;
     if (tok < 0 || tok >= lay.n_tok) tok = 0;
     a_off[i] = ((size_t)tok * hidden + (size_t)(((lane & 7) ^ (R & 7)) * 8)) * 2u;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int R = 32 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < NCB; ++i) {
+    const int R = 8 * NCB * wave + 8 * i + (lane >> 3);
     b_off[i] = ((uint32_t)R * (uint32_t)hidden + (uint32_t)(((lane & 7) ^ (R & 7)) * 8)) * 2u;
   }
   const unsigned char* xb = reinterpret_cast<const unsigned char*>(x);
@@ -119,19 +126,19 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
   // stage so each wait is a constant).
   auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
     const uint32_t kb = (uint32_t)min(kt, n_k - 1) * BK * 2u;
-    unsigned char* as = reinterpret_cast<unsigned char*>(&sm.st[slot].a[64 * wu][0]);
-    unsigned char* bs = reinterpret_cast<unsigned char*>(&sm.st[slot].b[32 * wu][0]);
+    unsigned char* as = reinterpret_cast<unsigned char*>(&sm.st[slot].a[8 * NCA * wu][0]);
+    unsigned char* bs = reinterpret_cast<unsigned char*>(&sm.st[slot].b[8 * NCB * wu][0]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NCA; ++i)
       __builtin_amdgcn_global_load_lds((gptr_t)(xb + a_off[i] + kb), (lptr_t)(as + i * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NCB; ++i)
       __builtin_amdgcn_global_load_lds((gptr_t)(wb + b_off[i] + kb), (lptr_t)(bs + i * 1024), 16, 0, 0);
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
@@ -142,16 +149,16 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
     const int slot = kt % NST2;
     // stage kt resident in every wave (stage kt+1's 12 copies may be in
     // flight); the slot of stage kt-1 is free for stage kt+2
-    asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NCA + NCB) : "memory");
     issue(kt + 2, (kt + 2) % NST2);
     const Gemm2Stage& S = sm.st[slot];
     // Operands of k-slice ks+1 are read while the MFMAs of slice ks run.
-    bf16x8 af[2][4], bfr[2][2];
+    bf16x8 af[2][MI], bfr[2][2];
     auto load = [&](int ks, int buf) __attribute__((always_inline)) {
       const int ch = 2 * ks + lh;              // 16-byte chunk of this lane's k range
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int R = wm * 128 + i * 32 + lr;
+      for (int i = 0; i < MI; ++i) {
+        const int R = wm * WROWS + i * 32 + lr;
         af[buf][i] = *reinterpret_cast<const bf16x8*>(&S.a[R][(ch ^ (R & 7)) * 8]);
       }
 #pragma unroll
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
       if (ks + 1 < BK / 16) load(ks + 1, (ks + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);     // keep those reads ahead of this slice's MFMAs
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
@@ -177,12 +184,12 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
 
   // ---- epilogue: fp32 tile -> LDS ------------------------------------------
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int r = wm * WROWS + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         const int c = wn * 64 + j * 32 + (lane & 31);
         sm.c[r][c] = acc[i][j][v];
       }
@@ -194,19 +201,19 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
     // entries, then rotating and storing.
     const bool is_q = head < hq;
     const int g = head - hq;
-    constexpr int kUnits = BM2 * 8 / 256;
+    constexpr int kUnits = BM2 * 8 / GT;
     const int c = tid & 7;
     f32x4 tabv[kUnits][4];
 #pragma unroll
     for (int k = 0; k < kUnits; ++k) {
-      const int m = (tid >> 3) + 32 * k;
+      const int m = (tid >> 3) + (GT / 8) * k;
       const f32x4* tab = reinterpret_cast<const f32x4*>(lay.rope_tab + (size_t)sm.row_pos[m] * 128 + c * 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) tabv[k][i] = tab[i];
     }
 #pragma unroll
     for (int k = 0; k < kUnits; ++k) {
-      const int m = (tid >> 3) + 32 * k;
+      const int m = (tid >> 3) + (GT / 8) * k;
       uint16_t* dst = nullptr;
       if (is_q) {
         if (q_out && sm.row_ok[m]) dst = q_out + ((size_t)(m0 + m) * hq + head) * 128;
@@ -237,12 +244,14 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm256_bf16(
     // V head: page layout [d][slot]; thread tid takes output row tid (all
     // 128 d of one token, 2-byte stores 32 bytes apart in its page).
     const int g = head - hq - hkv;
-    const int page = sm.row_page[tid];
+    constexpr int kDim = 128 * BM2 / GT;     // head dimensions per thread
+    const int row = tid % BM2, e0 = (tid / BM2) * kDim;
+    const int page = sm.row_page[row];
     if (page >= 0) {
-      uint16_t* base = vpool + ((size_t)page * hkv + g) * 128 * kPage + sm.row_slot[tid];
+      uint16_t* base = vpool + ((size_t)page * hkv + g) * 128 * kPage + sm.row_slot[row];
 #pragma unroll 4
-      for (int e = 0; e < 128; e += 4) {
-        const f32x4 c4 = *reinterpret_cast<const f32x4*>(&sm.c[tid][e]);
+      for (int e = e0; e < e0 + kDim; e += 4) {
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(&sm.c[row][e]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) base[(e + i) * kPage] = f2bf(c4[i]);
       }
@@ -446,7 +455,7 @@ sx_status launch_recompute(const sx_dims& dims, const sx_layout& lay, const void
     const size_t smem = sizeof(Gemm2Smem);
     const sx_status st = allow_lds((const void*)qkv_gemm256_bf16, smem, "sx_recompute_kv");
     if (st != SX_OK) return st;
-    qkv_gemm256_bf16<<<grid, 256, smem, stream>>>(
+    qkv_gemm256_bf16<<<grid, GT, smem, stream>>>(
         (const uint16_t*)x, dims.hidden, rows, n_rows, (const uint16_t*)w_qkv, head0, mt, n_heads,
         lay, kv.n_pages, (uint16_t*)kv.k, (uint16_t*)kv.v, (uint16_t*)q_out, hq, hkv);
   } else {
