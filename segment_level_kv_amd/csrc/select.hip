@@ -17,7 +17,9 @@
 // scores (-0 mapped to +0), a 4-pass 8-bit radix select for the k-th largest
 // key in LDS (per-wave histograms), then an in-order compaction sweep with
 // block prefix sums: all keys above the threshold plus the lowest-indexed
-// keys equal to it.  Output is ascending by token id.
+// keys equal to it.  Output is ascending by token id.  Every sweep issues a
+// batch of loads per thread before using them (one workgroup per request
+// would otherwise pay a memory round trip per element).
 #include "sx_device.hpp"
 #include "sx_internal.hpp"
 
@@ -89,35 +91,58 @@ __global__ __launch_bounds__(256) void scores_bf16(
 
   const int s0 = sq_start[req], s1 = sq_start[req + 1];
   float acc[2] = {0.f, 0.f};
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = g * G + hh;
-    for (int b0 = s0; b0 < s1; b0 += SQB) {
-      // Sparse-Q rows are ascending: skip blocks entirely before the tile.
-      const int last = min(b0 + SQB, s1) - 1;
-      if (sq_rows[last] - seq0 < k0) continue;
-      __syncthreads();
-      for (int u = tid; u < SQB * 16; u += 256) {
-        const int r = u >> 4, c = u & 15;
-        const int i = b0 + r;
-        u32x4 raw = {0, 0, 0, 0};
-        if (i < s1) {
-          const int qr = q_index ? q_index[i] : i;
-          raw = *reinterpret_cast<const u32x4*>(q + ((size_t)qr * hq + h) * 128 + c * 8);
-        }
-        *reinterpret_cast<u32x4*>(&sm.q[r][c * 8]) = raw;
+  // The Sparse-Q blocks that reach this key tile, visited head by head; the
+  // next block's Q rows, LSE and positions are loaded into registers while
+  // the current block is in the MFMAs.  Sparse-Q rows are ascending, so the
+  // blocks wholly before the tile form a prefix that is skipped.
+  int bfirst = s0;
+  while (bfirst < s1 && sq_rows[min(bfirst + SQB, s1) - 1] - seq0 < k0) bfirst += SQB;
+  const int n_blk = (s1 - bfirst + SQB - 1) / SQB;
+  const int n_it = n_blk * G;                // iteration it: head it / n_blk, block it % n_blk
+  constexpr int QU = SQB * 16 / 256;         // 16-byte Q chunks per thread and block
+  u32x4 qn[QU];
+  float lse_n = INFINITY;
+  int pos_n = -1;
+  auto fetch = [&](int it) __attribute__((always_inline)) {
+    const int h = g * G + it / n_blk;
+    const int b0 = bfirst + (it % n_blk) * SQB;
+#pragma unroll
+    for (int e = 0; e < QU; ++e) {
+      const int u = tid + 256 * e;
+      const int r = u >> 4, c = u & 15;
+      const int i = b0 + r;
+      qn[e] = u32x4{0, 0, 0, 0};
+      if (i < s1) {
+        const int qr = q_index ? q_index[i] : i;
+        qn[e] = *reinterpret_cast<const u32x4*>(q + ((size_t)qr * hq + h) * 128 + c * 8);
+      }
+    }
+    if (tid < SQB) {
+      const int i = b0 + tid;
+      lse_n = INFINITY;
+      pos_n = -1;
+      if (i < s1) {
+        const int lr = lse_index ? lse_index[i] : i;
+        lse_n = lse[(size_t)lr * hq + h] * kLog2e;
+        pos_n = sq_rows[i] - seq0;
+      }
+    }
+  };
+  if (n_it > 0) fetch(0);
+  for (int it = 0; it < n_it; ++it) {
+    {
+      __syncthreads();                        // every wave is done with the previous block
+#pragma unroll
+      for (int e = 0; e < QU; ++e) {
+        const int u = tid + 256 * e;
+        *reinterpret_cast<u32x4*>(&sm.q[u >> 4][(u & 15) * 8]) = qn[e];
       }
       if (tid < SQB) {
-        const int i = b0 + tid;
-        if (i < s1) {
-          const int lr = lse_index ? lse_index[i] : i;
-          sm.lse2[tid] = lse[(size_t)lr * hq + h] * kLog2e;
-          sm.qpos[tid] = sq_rows[i] - seq0;
-        } else {
-          sm.lse2[tid] = INFINITY;
-          sm.qpos[tid] = -1;
-        }
+        sm.lse2[tid] = lse_n;
+        sm.qpos[tid] = pos_n;
       }
       __syncthreads();
+      if (it + 1 < n_it) fetch(it + 1);
       f32x16 s[2] = {f32x16{}, f32x16{}};
       const uint16_t* qr = &sm.q[lane & 31][hl * 8];
 #pragma unroll
@@ -187,6 +212,7 @@ __global__ __launch_bounds__(256) void scores_f32(
 
 constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
+constexpr int TK_BATCH = 8;           // rounds of TK_THREADS tokens loaded together
 
 struct TopkSmem {
   uint32_t hist[TK_WAVES][256];
@@ -235,20 +261,61 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
   for (int i = 0; i < r; ++i) sel_off += max(k_sel[i], 0);
   const int k_req = max(k_sel[r], 0);
 
+  // Every loop below visits the request's tokens in batches of TK_BATCH per
+  // thread (token t0 + tid + TK_THREADS * (b + u)), issuing all the batch's
+  // loads before using any of them: a single workgroup would otherwise pay
+  // one memory round trip per element per thread.
+  constexpr int U = TK_BATCH;
+  const int n = t1 - t0;
+  const int n_rounds = (n + TK_THREADS - 1) / TK_THREADS;
+
   // pass 0: scores (fixed-order sum of the partial rows) and candidate count
   const float* src = partial;
   if (n_parts > 1 || scores != partial) {
-    for (int j = t0 + tid; j < t1; j += TK_THREADS) {
-      float s = 0.f;
-      for (int p = 0; p < n_parts; ++p) s += partial[(size_t)p * n_tok + j];
-      scores[j] = s;
+    for (int b = 0; b < n_rounds; b += U) {
+      float acc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[u] = 0.f;
+      for (int p = 0; p < n_parts; ++p) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = t0 + tid + TK_THREADS * (b + u);
+          v[u] = j < t1 ? partial[(size_t)p * n_tok + j] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] += v[u];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = t0 + tid + TK_THREADS * (b + u);
+        if (j < t1) scores[j] = acc[u];
+      }
     }
     src = scores;
     __threadfence_block();
     __syncthreads();
   }
+  // key and class of the batch starting at round b (class 2 past the end)
+  auto load_batch = [&](int b, uint32_t (&key)[U], int (&cls)[U]) __attribute__((always_inline)) {
+    float sv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = t0 + tid + TK_THREADS * (b + u);
+      cls[u] = j < t1 ? (int)tok_class[j] : 2;
+      sv[u] = j < t1 ? src[j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) key[u] = cls[u] == 0 ? order_key(sv[u]) : 0u;
+  };
   int my_cand = 0;
-  for (int j = t0 + tid; j < t1; j += TK_THREADS) my_cand += tok_class[j] == 0;
+  for (int b = 0; b < n_rounds; b += U) {
+    uint32_t key[U];
+    int cls[U];
+    load_batch(b, key, cls);
+#pragma unroll
+    for (int u = 0; u < U; ++u) my_cand += cls[u] == 0;
+  }
   int n_cand;
   block_scan(my_cand, sm, &n_cand);
   const int k = min(k_req, n_cand);
@@ -261,10 +328,13 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
       const int shift = 24 - 8 * pass;
       for (int i = tid; i < TK_WAVES * 256; i += TK_THREADS) (&sm.hist[0][0])[i] = 0;
       __syncthreads();
-      for (int j = t0 + tid; j < t1; j += TK_THREADS) {
-        if (tok_class[j] != 0) continue;
-        const uint32_t key = order_key(src[j]);
-        if ((key & pmask) == prefix) atomicAdd(&sm.hist[w][(key >> shift) & 255u], 1u);
+      for (int b = 0; b < n_rounds; b += U) {
+        uint32_t key[U];
+        int cls[U];
+        load_batch(b, key, cls);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (cls[u] == 0 && (key[u] & pmask) == prefix) atomicAdd(&sm.hist[w][(key[u] >> shift) & 255u], 1u);
       }
       __syncthreads();
       if (tid < 256) {
@@ -293,28 +363,33 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
   const uint32_t thr = prefix;       // key of the k-th largest candidate
   const int need_eq = remaining;     // how many keys equal to thr to take
 
-  // in-order compaction
+  // in-order compaction, one round of TK_THREADS tokens at a time (a batch
+  // of rounds loaded together)
   const int act_off = act_rows ? sq_start[r] + sel_off : 0;
   int base_eq = 0, base_sel = 0, base_act = 0;
-  for (int c0 = t0; c0 < t1; c0 += TK_THREADS) {
-    const int j = c0 + tid;
-    const bool valid = j < t1;
-    const int cls = valid ? tok_class[j] : 2;
-    const uint32_t key = (valid && cls == 0) ? order_key(src[j]) : 0u;
-    const bool cand = cls == 0 && k > 0;
-    const bool gt = cand && key > thr;
-    const bool eq = cand && key == thr;
-    int tot_eq;
-    const int eq_rank = base_eq + block_scan(eq ? 1 : 0, sm, &tot_eq);
-    const bool sel = gt || (eq && eq_rank < need_eq);
-    const bool act = sel || cls == 1;
-    int tot_pk;
-    const int pk = block_scan((sel ? 1 : 0) | (act ? 1 << 16 : 0), sm, &tot_pk);
-    if (sel) sel_rows[sel_off + base_sel + (pk & 0xffff)] = j;
-    if (act && act_rows) act_rows[act_off + base_act + (pk >> 16)] = j;
-    base_eq += tot_eq;
-    base_sel += tot_pk & 0xffff;
-    base_act += tot_pk >> 16;
+  for (int b = 0; b < n_rounds; b += U) {
+    uint32_t key[U];
+    int cls[U];
+    load_batch(b, key, cls);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (b + u >= n_rounds) break;                 // uniform across the workgroup
+      const int j = t0 + tid + TK_THREADS * (b + u);
+      const bool cand = cls[u] == 0 && k > 0;
+      const bool gt = cand && key[u] > thr;
+      const bool eq = cand && key[u] == thr;
+      int tot_eq;
+      const int eq_rank = base_eq + block_scan(eq ? 1 : 0, sm, &tot_eq);
+      const bool sel = gt || (eq && eq_rank < need_eq);
+      const bool act = sel || cls[u] == 1;
+      int tot_pk;
+      const int pk = block_scan((sel ? 1 : 0) | (act ? 1 << 16 : 0), sm, &tot_pk);
+      if (sel) sel_rows[sel_off + base_sel + (pk & 0xffff)] = j;
+      if (act && act_rows) act_rows[act_off + base_act + (pk >> 16)] = j;
+      base_eq += tot_eq;
+      base_sel += tot_pk & 0xffff;
+      base_act += tot_pk >> 16;
+    }
   }
   // budgets larger than the candidate count: pad with -1
   for (int i = k + tid; i < k_req; i += TK_THREADS) sel_rows[sel_off + i] = -1;
