@@ -122,7 +122,8 @@ def test_realign_parity_and_copy_semantics(shape):
 
 @pytest.mark.parametrize("shape,n_rows", [("llama", 300), ("qwen", 130), ("tiny", 40), ("llama", 1),
                                           ("llama", 16), ("llama", 17), ("qwen", 32), ("llama", 48),
-                                          ("qwen", 64), ("llama", 65)])
+                                          ("qwen", 64), ("llama", 65), ("qwen", 257),
+                                          ("llama", 513)])
 def test_recompute_parity_and_scatter(shape, n_rows):
     dims = SHAPES[shape]
     say(f"[recompute] shape={shape} rows={n_rows}")
