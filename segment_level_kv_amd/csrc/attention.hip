@@ -726,6 +726,17 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
   asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
 
   // ---- epilogue ----------------------------------------------------------------
+  // Final outputs go through LDS (the stage ring is free once every wave's
+  // copies have landed): each wave writes its 32 NB normalised bf16 output
+  // rows of 256 bytes there, then stores whole rows, 16 lanes per row, so
+  // HBM sees full lines instead of 8-byte pieces of 32 rows per instruction.
+  // Rows are padded to 272 bytes so the row-strided writes spread over the
+  // banks.
+  constexpr int kStgLd = 136;
+  static_assert(8 * 32 * kStgLd * 2 <= NSTAGE * (int)sizeof(Stage), "output staging fits the ring");
+  const bool final_out = it.slot < 0;
+  uint16_t* stg = reinterpret_cast<uint16_t*>(smem_raw) + (size_t)w * (32 * NB) * kStgLd;
+  if (WITH_O && final_out) __syncthreads();
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int p = 32 * NB * w + 32 * nb + (lane & 31);
@@ -737,9 +748,9 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
     const float m2 = m_run[nb] * c;                     // log2-domain max
     if (it.slot < 0) {
       if (lse && valid && hl == 0) lse[(size_t)m * hq + h] = (m2 + __log2f(l_tot)) * kLn2;
-      if (WITH_O && valid) {
+      if (WITH_O) {
         const float inv = 1.f / l_tot;
-        uint16_t* op = o + ((size_t)m * hq + h) * 128 + 4 * hl;
+        uint16_t* sp = stg + (32 * nb + (lane & 31)) * kStgLd + 4 * hl;
 #pragma unroll
         for (int md = 0; md < 4; ++md)
 #pragma unroll
@@ -747,7 +758,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
             u32x2 pk;
             pk[0] = pack_bf2(oacc[md][nb][4 * j] * inv, oacc[md][nb][4 * j + 1] * inv);
             pk[1] = pack_bf2(oacc[md][nb][4 * j + 2] * inv, oacc[md][nb][4 * j + 3] * inv);
-            *reinterpret_cast<u32x2*>(op + md * 32 + 8 * j) = pk;
+            *reinterpret_cast<u32x2*>(sp + md * 32 + 8 * j) = pk;
           }
       }
     } else if (it.slot < max_slots) {
@@ -768,6 +779,19 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
             pk[1] = pack_h2(oacc[md][nb][4 * j + 2] * inv, oacc[md][nb][4 * j + 3] * inv);
             *reinterpret_cast<u32x2*>(op + md * 32 + 8 * j) = pk;
           }
+      }
+    }
+  }
+  if (WITH_O && final_out) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's staging writes are done
+#pragma unroll
+    for (int i = 0; i < 8 * NB; ++i) {
+      const int pl = 4 * i + (lane >> 4), ch = lane & 15;
+      const int p = 32 * NB * w + pl;
+      if (p < npairs) {
+        const int r = p / G, hh = p - r * G;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + pl * kStgLd + ch * 8);
+        *reinterpret_cast<u32x4*>(o + ((size_t)(it.row0 + r) * hq + g * G + hh) * 128 + ch * 8) = v;
       }
     }
   }
