@@ -120,6 +120,17 @@ def test_layer_llama_bf16_context_dependent_caches():
     _check_case(synth.llama_layer_case(n_seg=3, cache_noise=0.5, ratio=(30, 100)))
 
 
+@pytest.mark.parametrize("ratio", [(0, 100), (100, 100)])
+def test_layer_llama_bf16_extreme_ratios(ratio):
+    """bf16, Llama shapes: at 0% only the new rows are recomputed and attend
+    over the realigned cache; at 100% every reused row is recomputed and
+    attends, i.e. a full prefill of the same rows."""
+    run = _check_case(synth.llama_layer_case(n_seg=3, cache_noise=0.5, ratio=ratio))
+    T = int(run.plan["seq_start"][1])
+    n_act = len(run.act_rows)
+    assert n_act == (T if ratio[0] == 100 else 256)
+
+
 def test_layer_agent_batch_fallback_bf16():
     """Several requests, no new tokens: the tail fallback supplies I_nr."""
     case = synth.agent_case(n_req=3, target=2500, n_pool=10, lmax=512)
