@@ -8,29 +8,31 @@
 // ------------------
 // Work unit: one kv head g and one query tile of (row, head) pairs: M
 // consecutive active rows of one request times the G query heads of g
-// (M = 256 / G, so a tile is at most 256 pairs, 64 per wave).  Long tiles
-// are split along the key axis into chunks so that every compute unit gets
-// several units of similar length; each chunk is one workgroup.  A small
+// (M = 256 / G, so a tile is at most 256 pairs: 8 waves of 32, two waves per
+// SIMD).  Tiles are split along the key axis into chunks only when there are
+// fewer tiles than compute units; each chunk is one workgroup.  A small
 // single-workgroup kernel builds the list of (tile, key chunk) items on the
 // device (the active rows are device data) and orders it longest first; a
 // merge kernel combines the chunks of split tiles in chunk order, so results
 // do not depend on scheduling.
 //
-// Per 64-key block and wave (64 pairs):
-//   S^T[key][pair] = K . Q^T    32 x v_mfma_f32_32x32x16_bf16, Q in registers
-//   online softmax over the key axis, which lies inside a lane (32 keys per
-//   lane and pair, the other 32 in the partner lane half)
-//   O^T[d][pair] += V^T . P^T   32 x v_mfma_f32_32x32x16_bf16
-// Keys are permuted inside each 32-key block when K is read from LDS so that
-// the S^T accumulators are directly the B operand of the PV product.  The
-// QK^T product of block j+1 is issued before the softmax of block j so that
-// its MFMAs overlap the exponentials.  The running maximum is raised only
-// when a block's maximum exceeds it by more than 2^8 (in the exp2 domain),
-// so O is rarely rescaled; exp2 arguments then stay below 8.
-// K/V blocks stream through a 3-stage LDS ring (one barrier per block);
-// the page ids of a block are wave-uniform and come through the scalar
-// cache.  Workgroup b takes kv head b % Hkv: with 8 kv heads each XCD streams
-// one head's K/V through its own L2.
+// Per 32-key sub-block and wave (32 pairs):
+//   S^T[key][pair] = K . Q^T    8 x v_mfma_f32_32x32x16_bf16, Q in AGPRs
+//   online softmax over the key axis, which lies inside a lane (16 keys per
+//   lane and pair, the other 16 in the partner lane half)
+//   O^T[d][pair] += V^T . P^T   8 x v_mfma_f32_32x32x16_bf16
+// Keys are permuted inside each 32-key sub-block when K is read from LDS so
+// that the S^T accumulators are directly the B operand of the PV product.
+// A step issues QK^T of sub-block j+2, PV of j and the softmax of j+1, which
+// are independent; the two waves of a SIMD run the MFMA and softmax phases
+// in opposite orders.  The running maximum is raised only when a block's
+// maximum exceeds it by more than 2^8 (in the exp2 domain), so O is rarely
+// rescaled; exp2 arguments then stay below 8.
+// K/V stream through a 4-stage LDS ring of 64-key stages (global -> LDS
+// directly, one barrier per stage); the page ids of a stage are
+// wave-uniform and come through the scalar cache.  Workgroup b takes kv head
+// b % Hkv: with 8 kv heads each XCD streams one head's K/V through its own
+// L2.  Final outputs leave through LDS as whole 256-byte rows.
 #include <type_traits>
 
 #include "sx_device.hpp"
