@@ -114,6 +114,29 @@ def decode_measure(run, dims, n_layers: int, t: int, reps: int = 5):
             "calls_timed": reps * len(layers)}
 
 
+def mfma_peak_measure(n_wg: int = 2048, iters: int = 400, reps: int = 5):
+    """Measured bf16 MFMA throughput (sx_mfma_peak_probe: back-to-back
+    v_mfma_f32_32x32x16_bf16 on every compute unit), timed with events on the
+    launch stream; outside the timed prefill steps."""
+    import torch
+    from segment_level_kv_amd import _lib as L
+    out = torch.empty(n_wg * 8, dtype=torch.float32, device="cuda")
+    L.sx_mfma_peak_probe(n_wg, iters, out)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        L.sx_mfma_peak_probe(n_wg, iters, out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = float(n_wg) * 8 * iters * 16 * 32768
+    return {"kernel": "sx_mfma_peak_probe (v_mfma_f32_32x32x16_bf16, 8 waves per workgroup)",
+            "workgroups": n_wg, "ms_per_launch": round(ms, 4),
+            "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1), "spec_TFLOP/s": PEAK_BF16_TFLOPS}
+
+
 def cpu_baseline(dims, plan, n_sparse: int, T: int, reused: int, seed: int = 4242):
     """The float64 oracle on a bounded sample of one sparse layer of the same
     workload, scaled to tokens/s per layer.  Sample: realign of one
@@ -362,6 +385,9 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     out["decode_attn"] = decode_measure(run, dims, n_layers, t)
+    peak = mfma_peak_measure()
+    out["mfma_peak_measured"] = peak
+    out["attn_pct_measured_mfma_peak"] = round(100.0 * achieved / peak["TFLOP/s"], 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(dims, run.plan, n_sparse, T, reused)
     print(json.dumps(out), flush=True)

@@ -30,7 +30,7 @@ CFLAGS = [
     "-Wall", "-Wno-unused-result",
 ]
 SOURCES = ["api.cpp", "seg_index.cpp", "rope_realign.hip", "recompute_kv.hip", "attention.hip",
-           "select.hip", "decode.hip"]
+           "select.hip", "decode.hip", "mfma_peak.hip"]
 # Per-source extra flags.  The attention softmax never produces NaN (masked
 # logits are -inf), so max reductions need no NaN quieting.  Compiler-selected
 # MFMAs in attention write VGPRs (the score tiles the softmax reads); the

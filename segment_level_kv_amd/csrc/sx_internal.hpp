@@ -60,4 +60,7 @@ sx_status launch_topk(const float* partial, int n_parts, const uint8_t* tok_clas
                       const int32_t* sq_start, int32_t* sel_rows, int32_t* act_rows,
                       float* scores_out, void* ws, hipStream_t stream);
 
+// Back-to-back bf16 MFMAs on every compute unit (measured-peak probe).
+sx_status launch_mfma_peak(int n_workgroups, int iters, float* out, hipStream_t stream);
+
 }  // namespace sx

@@ -80,6 +80,11 @@ def test_validation_errors_launch_nothing():
     assert lib.sx_recompute_kv(C.byref(d), C.byref(bad_lay), FAKE, FAKE, 1, FAKE, C.byref(pages), None,
                                None) == L.SX_EINVAL
     assert lib.sx_topk(None, FAKE, FAKE, 1, 4, FAKE, FAKE, None, 0, None) == L.SX_EINVAL
+    # MFMA probe: sizes and output are checked before any launch
+    assert lib.sx_mfma_peak_probe(0, 10, FAKE, None) == L.SX_EINVAL
+    assert lib.sx_mfma_peak_probe(4, 0, FAKE, None) == L.SX_EINVAL
+    assert lib.sx_mfma_peak_probe(4, 10, None, None) == L.SX_EINVAL
+    assert "sx_mfma_peak_probe" in L.last_error()
 
 
 def test_zero_sized_calls_are_noops():
