@@ -114,27 +114,33 @@ def decode_measure(run, dims, n_layers: int, t: int, reps: int = 5):
             "calls_timed": reps * len(layers)}
 
 
-def mfma_peak_measure(n_wg: int = 2048, iters: int = 400, reps: int = 5):
+def mfma_peak_measure(shapes=((2048, 400), (4096, 200), (8192, 100)), reps: int = 5):
     """Measured bf16 MFMA throughput (sx_mfma_peak_probe: back-to-back
     v_mfma_f32_32x32x16_bf16 on every compute unit), timed with events on the
-    launch stream; outside the timed prefill steps."""
+    launch stream, outside the timed prefill steps.  The best of a few launch
+    shapes is the measured peak (the highest rate the chip was seen to
+    sustain, so fractions against it are not flattered)."""
     import torch
     from segment_level_kv_amd import _lib as L
-    out = torch.empty(n_wg * 8, dtype=torch.float32, device="cuda")
-    L.sx_mfma_peak_probe(n_wg, iters, out)
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
+    rates = []
+    for n_wg, iters in shapes:
+        out = torch.empty(n_wg * 8, dtype=torch.float32, device="cuda")
         L.sx_mfma_peak_probe(n_wg, iters, out)
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
-    flops = float(n_wg) * 8 * iters * 16 * 32768
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            L.sx_mfma_peak_probe(n_wg, iters, out)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        flops = float(n_wg) * 8 * iters * 16 * 32768
+        rates.append({"workgroups": n_wg, "iters": iters, "ms_per_launch": round(ms, 4),
+                      "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)})
+    best = max(r["TFLOP/s"] for r in rates)
     return {"kernel": "sx_mfma_peak_probe (v_mfma_f32_32x32x16_bf16, 8 waves per workgroup)",
-            "workgroups": n_wg, "ms_per_launch": round(ms, 4),
-            "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1), "spec_TFLOP/s": PEAK_BF16_TFLOPS}
+            "TFLOP/s": best, "shapes": rates, "spec_TFLOP/s": PEAK_BF16_TFLOPS}
 
 
 def cpu_baseline(dims, plan, n_sparse: int, T: int, reused: int, seed: int = 4242):
