@@ -235,3 +235,38 @@ def test_sampled_output_rows_equal_the_full_computation():
     assert np.array_equal(given["O_exact"], full["O_exact"][[1, 3]])
     with pytest.raises(ValueError):
         _run(case, (1, 3), out_rows=[int(np.setdiff1d(np.arange(plan["T"]), full["A"])[0])])
+
+
+@pytest.mark.parametrize("t", [0, 1, 3])
+def test_stack_with_every_token_recomputed_is_full_prefill(t):
+    """Pin P12 at the stack level: three layers, each with its own inputs
+    and context-dependent caches, threshold t.  Layers below t are full; the
+    boundary selection takes layer t-1's probabilities (or, for t = 0, the
+    probe of layer 0) at ratio 100%, so it selects every candidate, and every
+    sparse layer then equals a full prefill of its own inputs.  t = 3 is the
+    all-full stack."""
+    n_layers = 3
+    cases = [_case(SMALL_F32, LAYOUT, LENS, seed=40 + l, noise=0.5) for l in range(n_layers)]
+    plan = oracle.plan_request(cases[0].piece_lengths(0), (1, 1))
+    d = SMALL_F32
+    S = None
+    for l, case in enumerate(cases):
+        ref = _straight_full_prefill(case)
+        if l < t:
+            full = oracle.full_layer(case.request_x(0), case.wq, case.wk, case.wv, d.theta,
+                                     d.n_q_heads, d.n_kv_heads, d.head_dim, d.dtype)
+            assert np.max(np.abs(full["O_exact"] - ref)) < 1e-9
+            if l == t - 1:
+                sq = plan["sq"]
+                scores = oracle.attention_mass_scores(full["q"][sq], sq, full["K"], full["lse"][sq])
+                S = oracle.select_topk(scores, plan["cand"], plan["k"])
+                assert np.array_equal(S, np.sort(plan["cand"]))
+        else:
+            segs = _build_caches(case, 0)
+            out = oracle.sparse_layer(case.request_x(0), case.wq, case.wk, case.wv, plan, segs,
+                                      d.theta, d.n_q_heads, d.n_kv_heads, d.head_dim, d.dtype,
+                                      selected=S)
+            if S is None:
+                S = out["S"]
+            assert len(out["A"]) == plan["T"]
+            assert np.max(np.abs(out["O_exact"] - ref)) < 1e-9
