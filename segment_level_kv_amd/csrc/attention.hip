@@ -924,9 +924,13 @@ sx_status launch_bf16(const sx_dims& dims, const sx_layout& lay, const void* q,
   uint16_t* part_o = WITH_O ? reinterpret_cast<uint16_t*>(base + L.part_o) : nullptr;
   const int M = rows_per_tile(G);
   const int target = items_per_head(hkv);
+  // Every request's rows are tiled separately, so there are at least
+  // n_rows / M tiles: with n_rows >= M * target no tile is split, the work
+  // list is told so (allow_split = 0) and the merge pass is not launched.
+  const bool may_split = (long long)n_rows < (long long)M * target;
   build_work<<<1, kBuildThreads, (size_t)(lay.n_req + 1) * sizeof(int), stream>>>(row_start, rows, lay.seq_start, lay.n_req, n_rows, M,
-                                              target, L.max_tiles, L.max_items, 1, tiles, items,
-                                              merges, counters);
+                                              target, L.max_tiles, L.max_items, may_split ? 1 : 0,
+                                              tiles, items, merges, counters);
   sx_status st = check_launch("attention work list");
   if (st != SX_OK) return st;
   const size_t smem = NSTAGE * sizeof(Stage);
@@ -939,6 +943,7 @@ sx_status launch_bf16(const sx_dims& dims, const sx_layout& lay, const void* q,
       L.max_items, scale_log2);
   st = check_launch("attention");
   if (st != SX_OK) return st;
+  if (!may_split) return SX_OK;
   attn_merge<WITH_O><<<L.max_tiles * hkv * (PAIRS / kMergePairs), 256, 0, stream>>>(merges, counters, hkv, G, part_ml,
                                                            part_o, (uint16_t*)o, lse, L.max_items);
   return check_launch("attention merge");
