@@ -366,7 +366,7 @@ def main():
         },
         "attn_pct_mfma_bf16_peak": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
         "roofline": {
-            "kernel": "sx_sparse_attn (build_work + attn_fwd<true,1> + attn_merge)",
+            "kernel": "sx_sparse_attn (build_work + attn_fwd<true,1>; attn_merge only when tiles are split)",
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
