@@ -95,7 +95,8 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
   }
 
   // ---- copy plan: lane L of copy i moves one 16-byte chunk --------------
-  // A: rows 64*wave + 8*i + L/8 (i < 8); B: rows 32*wave + 8*i + L/8 (i < 4).
+  // A: rows 8*NCA*wave + 8*i + L/8 (i < NCA); B: rows 8*NCB*wave + 8*i + L/8
+  // (i < NCB).
   // Row R's chunk c is stored at chunk position c ^ (R & 7) = L % 8, so the
   // lane loads chunk (L % 8) ^ (R & 7).  Rows past n_rows (or with a token
   // outside the sequence) read row 0 of x: finite data whose results are
@@ -122,8 +123,8 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
   const int wu = __builtin_amdgcn_readfirstlane(wave);
   const int n_k = hidden / BK;
   // Stage kt (k = 64 kt, clamped to the last step: the copies past the end
-  // repeat it into a ring slot no one reads any more, keeping 12 copies per
-  // stage so each wait is a constant).
+  // repeat it into a ring slot no one reads any more, keeping NCA + NCB
+  // copies per wave and stage so each wait is a constant).
   auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
     const uint32_t kb = (uint32_t)min(kt, n_k - 1) * BK * 2u;
     unsigned char* as = reinterpret_cast<unsigned char*>(&sm.st[slot].a[8 * NCA * wu][0]);
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
   issue(1, 1);
   for (int kt = 0; kt < n_k; ++kt) {
     const int slot = kt % NST2;
-    // stage kt resident in every wave (stage kt+1's 12 copies may be in
+    // stage kt resident in every wave (stage kt+1's copies may be in
     // flight); the slot of stage kt-1 is free for stage kt+2
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NCA + NCB) : "memory");
     issue(kt + 2, (kt + 2) % NST2);
@@ -241,8 +242,8 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
       }
     }
   } else {
-    // V head: page layout [d][slot]; thread tid takes output row tid (all
-    // 128 d of one token, 2-byte stores 32 bytes apart in its page).
+    // V head: page layout [d][slot]; thread tid takes output row tid % 256
+    // and half of its 128 d (2-byte stores 32 bytes apart in its page).
     const int g = head - hq - hkv;
     constexpr int kDim = 128 * BM2 / GT;     // head dimensions per thread
     const int row = tid % BM2, e0 = (tid / BM2) * kDim;
