@@ -390,6 +390,30 @@ def main():
         "full_layer_ms": round(full_rec_ms + full_attn_ms, 4),
         "wall_s_timed": round(wall, 3),
     }
+    # every kernel of the sparse layer (and the full layer) against its roofline,
+    # per launch; the selection's work is the QK^T of the Sparse-Q rows over
+    # their key prefixes, once for the LSE probe and once for the scores
+    sq = np.asarray(run.plan["sq_rows"], dtype=np.int64) - int(run.seq_start_h[0])
+    sel_flops = 2 * (2.0 * dims.head_dim * dims.n_q_heads * float(np.sum(sq + 1)))
+    full_rec_flops = 2.0 * T * dims.qkv_rows * dims.hidden
+    rate = lambda work, ms, unit: round(work / (ms * 1e-3) / unit, 1) if ms else None
+    out["kernels"] = {
+        "realign": {"GB/s": rate(realign_bytes, realign_ms, 1e9), "peak": PEAK_HBM_GBS,
+                    "frac": round(realign_bytes / (realign_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "recompute_active": {"TFLOP/s": rate(rec_flops, rec_ms, 1e12), "peak": PEAK_BF16_TFLOPS,
+                             "frac": round(rec_flops / (rec_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "sparse_attn": {"TFLOP/s": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                        "frac": round(achieved / PEAK_BF16_TFLOPS, 4)},
+        "select": {"TFLOP/s": rate(sel_flops, sel_ms, 1e12), "peak": PEAK_BF16_TFLOPS,
+                   "frac": round(sel_flops / (sel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4) if sel_ms else None},
+        "full_recompute": {"TFLOP/s": rate(full_rec_flops, full_rec_ms, 1e12), "peak": PEAK_BF16_TFLOPS,
+                           "frac": round(full_rec_flops / (full_rec_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4) if full_rec_ms else None},
+        "full_attn": {"TFLOP/s": rate(full_attn_flops, full_attn_ms, 1e12), "peak": PEAK_BF16_TFLOPS,
+                      "frac": round(full_attn_flops / (full_attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4) if full_attn_ms else None},
+    }
+    out["active_rows_per_s_per_layer"] = round(run.n_act / (t_layer_ms * 1e-3), 1)
+    if full_rec_ms and full_attn_ms:
+        out["speedup_vs_full_layer"] = round((full_rec_ms + full_attn_ms) / t_layer_ms, 2)
     out["decode_attn"] = decode_measure(run, dims, n_layers, t)
     peak = mfma_peak_measure()
     out["mfma_peak_measured"] = peak
