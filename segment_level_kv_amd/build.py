@@ -33,9 +33,11 @@ SOURCES = ["api.cpp", "seg_index.cpp", "rope_realign.hip", "recompute_kv.hip", "
            "select.hip", "decode.hip", "mfma_peak.hip"]
 # Per-source extra flags.  The attention softmax never produces NaN (masked
 # logits are -inf), so max reductions need no NaN quieting.  Compiler-selected
-# MFMAs in attention write VGPRs (the score tiles the softmax reads); the
-# output accumulators are kept in AGPRs by the kernel's own asm.
-EXTRA = {"attention.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# MFMAs in attention and in the selection's score pass write VGPRs (the score
+# tiles the VALU reads next); attention keeps its output accumulators in
+# AGPRs by its own asm.
+EXTRA = {"attention.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "select.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -157,7 +157,9 @@ __global__ __launch_bounds__(256) void scores_bf16(
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int qr_ = 8 * (v >> 2) + 4 * hl + (v & 3);
-          const float p = exp2f(s[nb][v] * scale_log2 - sm.lse2[qr_]);
+          // v_exp_f32 directly: the argument is a log2 probability (<= 0 up to
+          // rounding); below 2^-126 the term is below any score tolerance.
+          const float p = __builtin_amdgcn_exp2f(s[nb][v] * scale_log2 - sm.lse2[qr_]);
           acc[nb] += (sm.qpos[qr_] >= key_idx[nb]) ? p : 0.f;
         }
     }
