@@ -323,7 +323,7 @@ def main():
     t_layer_ms = sparse_wall_ms / n_sparse
     value = T / (t_layer_ms * 1e-3)
     phase_sum_ms = (ph.get("realign", 0) + ph.get("recompute", 0) + ph.get("sparse_attn", 0)
-                    + ph.get("select", 0)) / K / n_sparse
+                    + ph.get("select", 0) + ph.get("attn_plan", 0)) / K / n_sparse
 
     # sparse attention roofline: unmasked MACs of QK^T and PV
     act = run.act_rows[:run.n_act].cpu().numpy().astype(np.int64)
@@ -342,6 +342,7 @@ def main():
     full_attn_ms = ph.get("full_attn", 0) / max(cnt.get("full_attn", 1), 1)
     full_attn_flops = 4.0 * dims.head_dim * dims.n_q_heads * (T * (T + 1) / 2)
     sel_ms = ph.get("select", 0) / max(cnt.get("select", 1), 1)
+    plan_ms = ph.get("attn_plan", 0) / max(cnt.get("attn_plan", 1), 1)
 
     out = {
         "metric": METRIC,
@@ -366,7 +367,8 @@ def main():
         },
         "attn_pct_mfma_bf16_peak": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
         "roofline": {
-            "kernel": "sx_sparse_attn (build_work + attn_fwd<true,1>; attn_merge only when tiles are split)",
+            "kernel": ("sx_sparse_attn_run (attn_fwd<true,1>; attn_merge only when tiles are split), one "
+                       "launch per sparse layer over the work list sx_sparse_attn_plan builds once per pass"),
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
@@ -374,7 +376,7 @@ def main():
         },
         "phases_ms_per_launch": {
             "realign": round(realign_ms, 4), "recompute_active": round(rec_ms, 4),
-            "sparse_attn": round(attn_ms, 4), "select": round(sel_ms, 4),
+            "sparse_attn": round(attn_ms, 4), "select": round(sel_ms, 4), "attn_plan": round(plan_ms, 4),
             "full_recompute": round(full_rec_ms, 4), "full_attn": round(full_attn_ms, 4),
         },
         "phases_rate": {

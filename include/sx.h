@@ -357,6 +357,27 @@ sx_status sx_sparse_attn(const sx_dims *dims, const sx_layout *lay, const void *
                          const sx_pages *kv, void *o, float *lse, void *ws, size_t ws_bytes,
                          void *stream);
 
+/* sx_sparse_attn in two calls, for callers that attend over the same active
+ * rows in many layers (after the boundary selection of §3.4 the set
+ * A = I_nr U S is fixed for every later layer).
+ * sx_sparse_attn_plan: the work list of the attention over rows / row_start
+ *   (as for sx_sparse_attn), written into ws; only ws is written.
+ * sx_sparse_attn_run: sx_sparse_attn over the work list already in ws.
+ *   dims, lay, rows, row_start's content and n_rows must be those the plan
+ *   was built for, and ws must not have been written in between (by this
+ *   library or the caller); any number of runs may follow one plan, with any
+ *   q, kv, o and lse.  Violations give unspecified outputs (in-bounds
+ *   accesses only).  sx_sparse_attn(...) equals the plan followed by a run
+ *   and gives the same bits.
+ * ws: sx_workspace_bytes(SX_OP_SPARSE_ATTN, ...) bytes for both.  Errors as
+ * for sx_sparse_attn. */
+sx_status sx_sparse_attn_plan(const sx_dims *dims, const sx_layout *lay, const int32_t *rows,
+                              const int32_t *row_start, int32_t n_rows, void *ws, size_t ws_bytes,
+                              void *stream);
+sx_status sx_sparse_attn_run(const sx_dims *dims, const sx_layout *lay, const void *q,
+                             const int32_t *rows, int32_t n_rows, const sx_pages *kv, void *o,
+                             float *lse, void *ws, size_t ws_bytes, void *stream);
+
 /* Full causal prefill attention of every token (the layers before the
  * threshold, §3.4): sx_sparse_attn with rows = 0..n_tok-1.  q: [n_tok][Hq][d],
  * o: [n_tok][Hq*d], lse: [n_tok][Hq] or NULL. */

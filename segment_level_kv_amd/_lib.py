@@ -23,7 +23,7 @@ SX_OP_REALIGN, SX_OP_RECOMPUTE, SX_OP_SELECT, SX_OP_TOPK, SX_OP_SPARSE_ATTN, SX_
 EXPORTED = [
     "sx_rope_table", "sx_plan_layout", "sx_plan_realign", "sx_realign_jobs_bound",
     "sx_workspace_bytes", "sx_rope_realign", "sx_recompute_kv", "sx_select_topk", "sx_topk",
-    "sx_sparse_attn", "sx_full_attn", "sx_decode_attn", "sx_mfma_peak_probe", "sx_last_error",
+    "sx_sparse_attn", "sx_sparse_attn_plan", "sx_sparse_attn_run", "sx_full_attn", "sx_decode_attn", "sx_mfma_peak_probe", "sx_last_error",
     "sx_virtual_hash", "sx_index_create", "sx_index_destroy", "sx_index_alloc", "sx_index_release",
     "sx_index_insert", "sx_index_lookup", "sx_index_remove", "sx_index_stats", "sx_plan_segments",
 ]
@@ -83,6 +83,8 @@ def lib():
             "sx_select_topk": (I, [P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, Z, P]),
             "sx_topk": (I, [P, P, P, I, I, P, P, P, Z, P]),
             "sx_sparse_attn": (I, [P, P, P, P, P, I, P, P, P, P, Z, P]),
+            "sx_sparse_attn_plan": (I, [P, P, P, P, I, P, Z, P]),
+            "sx_sparse_attn_run": (I, [P, P, P, P, I, P, P, P, P, Z, P]),
             "sx_full_attn": (I, [P, P, P, P, P, P, P, Z, P]),
             "sx_decode_attn": (I, [P, P, P, P, P, P, P, Z, P]),
             "sx_mfma_peak_probe": (I, [I, I, P, P]),
@@ -325,6 +327,20 @@ def sx_sparse_attn(dims: Dims, lay: Layout, q, rows, row_start, n_rows: int, kv:
     _check(lib().sx_sparse_attn(_ref(dims), _ref(lay), _ptr(q), _ptr(rows), _ptr(row_start),
                                 n_rows, _ref(kv), _ptr(o), _ptr(lse), _ptr(ws), ws_bytes,
                                 _stream(stream)), "sx_sparse_attn")
+
+
+def sx_sparse_attn_plan(dims: Dims, lay: Layout, rows, row_start, n_rows: int, ws, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sx_sparse_attn_plan(_ref(dims), _ref(lay), _ptr(rows), _ptr(row_start), n_rows,
+                                     _ptr(ws), ws_bytes, _stream(stream)), "sx_sparse_attn_plan")
+
+
+def sx_sparse_attn_run(dims: Dims, lay: Layout, q, rows, n_rows: int, kv: Pages, o, lse, ws,
+                       stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sx_sparse_attn_run(_ref(dims), _ref(lay), _ptr(q), _ptr(rows), n_rows, _ref(kv),
+                                    _ptr(o), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)),
+           "sx_sparse_attn_run")
 
 
 def sx_decode_attn(dims: Dims, lay: Layout, q, kv: Pages, o, lse, ws, stream=None):

@@ -306,6 +306,37 @@ sx_status sx_sparse_attn(const sx_dims* dims, const sx_layout* lay, const void* 
                           as_stream(stream));
 }
 
+sx_status sx_sparse_attn_plan(const sx_dims* dims, const sx_layout* lay, const int32_t* rows,
+                              const int32_t* row_start, int32_t n_rows, void* ws, size_t ws_bytes,
+                              void* stream) {
+  const char* fn = "sx_sparse_attn_plan";
+  SX_TRY(check_dims(dims, fn));
+  SX_TRY(check_layout(lay, fn));
+  SX_REQUIRE(n_rows >= 0, SX_EINVAL, "%s: n_rows < 0", fn);
+  if (n_rows == 0) return SX_OK;
+  SX_REQUIRE(rows && row_start, SX_EINVAL, "%s: rows/row_start is NULL", fn);
+  const size_t need = sx_workspace_bytes(SX_OP_SPARSE_ATTN, dims, lay->n_tok, n_rows, lay->n_req);
+  SX_REQUIRE(need == 0 || (ws && ws_bytes >= need), SX_EWORKSPACE,
+             "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : (size_t)0);
+  return launch_attention_plan(*dims, *lay, rows, row_start, n_rows, ws, as_stream(stream));
+}
+
+sx_status sx_sparse_attn_run(const sx_dims* dims, const sx_layout* lay, const void* q,
+                             const int32_t* rows, int32_t n_rows, const sx_pages* kv, void* o,
+                             float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "sx_sparse_attn_run";
+  SX_TRY(check_dims(dims, fn));
+  SX_TRY(check_layout(lay, fn));
+  SX_TRY(check_pages(kv, fn, "kv"));
+  SX_REQUIRE(n_rows >= 0, SX_EINVAL, "%s: n_rows < 0", fn);
+  if (n_rows == 0) return SX_OK;
+  SX_REQUIRE(q && rows && o, SX_EINVAL, "%s: q/rows/o is NULL", fn);
+  const size_t need = sx_workspace_bytes(SX_OP_SPARSE_ATTN, dims, lay->n_tok, n_rows, lay->n_req);
+  SX_REQUIRE(need == 0 || (ws && ws_bytes >= need), SX_EWORKSPACE,
+             "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : (size_t)0);
+  return launch_attention_run(*dims, *lay, q, nullptr, rows, n_rows, *kv, o, lse, ws, as_stream(stream));
+}
+
 sx_status sx_full_attn(const sx_dims* dims, const sx_layout* lay, const void* q, const sx_pages* kv,
                        void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "sx_full_attn";

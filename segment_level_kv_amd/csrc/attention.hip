@@ -908,33 +908,44 @@ __global__ __launch_bounds__(64) void attn_rows_f32(
   if (lse && lane == 0) lse[(size_t)m * hq + h] = m_run + logf(l_run);
 }
 
+// Whether a work list over n_rows rows can hold split tiles.  Every
+// request's rows are tiled separately, so there are at least n_rows / M
+// tiles: with n_rows >= M * target no tile is split (the work list is told
+// so) and the merge pass is not launched.
+bool attn_may_split(int n_rows, int G, int hkv) {
+  return (long long)n_rows < (long long)rows_per_tile(G) * items_per_head(hkv);
+}
+
+// The work list (tiles, items, merges, counters) into ws.  Its offsets in
+// ws do not depend on whether outputs are produced.
+sx_status plan_bf16(const sx_dims& dims, const sx_layout& lay, const int32_t* rows,
+                    const int32_t* row_start, int n_rows, void* ws, hipStream_t stream) {
+  const int hq = dims.n_q_heads, hkv = dims.n_kv_heads, G = hq / hkv;
+  const WsLayout L = ws_layout(n_rows, lay.n_req, G, hkv, true);
+  char* base = static_cast<char*>(ws);
+  build_work<<<1, kBuildThreads, (size_t)(lay.n_req + 1) * sizeof(int), stream>>>(
+      row_start, rows, lay.seq_start, lay.n_req, n_rows, rows_per_tile(G), items_per_head(hkv),
+      L.max_tiles, L.max_items, attn_may_split(n_rows, G, hkv) ? 1 : 0,
+      reinterpret_cast<TileInfo*>(base + L.tiles), reinterpret_cast<AttnItem*>(base + L.items),
+      reinterpret_cast<MergeTile*>(base + L.merges), reinterpret_cast<int32_t*>(base + L.counters));
+  return check_launch("attention work list");
+}
+
+// Attention and merge over the work list already in ws.
 template <bool WITH_O>
-sx_status launch_bf16(const sx_dims& dims, const sx_layout& lay, const void* q,
-                      const int32_t* q_index, const int32_t* rows, const int32_t* row_start,
-                      int n_rows, const sx_pages& kv, void* o, float* lse, void* ws,
-                      hipStream_t stream) {
+sx_status run_bf16(const sx_dims& dims, const sx_layout& lay, const void* q,
+                   const int32_t* q_index, const int32_t* rows, int n_rows, const sx_pages& kv,
+                   void* o, float* lse, void* ws, hipStream_t stream) {
   const int hq = dims.n_q_heads, hkv = dims.n_kv_heads, G = hq / hkv;
   const WsLayout L = ws_layout(n_rows, lay.n_req, G, hkv, WITH_O);
   char* base = static_cast<char*>(ws);
   int32_t* counters = reinterpret_cast<int32_t*>(base + L.counters);
-  TileInfo* tiles = reinterpret_cast<TileInfo*>(base + L.tiles);
   AttnItem* items = reinterpret_cast<AttnItem*>(base + L.items);
   MergeTile* merges = reinterpret_cast<MergeTile*>(base + L.merges);
   float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
   uint16_t* part_o = WITH_O ? reinterpret_cast<uint16_t*>(base + L.part_o) : nullptr;
-  const int M = rows_per_tile(G);
-  const int target = items_per_head(hkv);
-  // Every request's rows are tiled separately, so there are at least
-  // n_rows / M tiles: with n_rows >= M * target no tile is split, the work
-  // list is told so (allow_split = 0) and the merge pass is not launched.
-  const bool may_split = (long long)n_rows < (long long)M * target;
-  build_work<<<1, kBuildThreads, (size_t)(lay.n_req + 1) * sizeof(int), stream>>>(row_start, rows, lay.seq_start, lay.n_req, n_rows, M,
-                                              target, L.max_tiles, L.max_items, may_split ? 1 : 0,
-                                              tiles, items, merges, counters);
-  sx_status st = check_launch("attention work list");
-  if (st != SX_OK) return st;
   const size_t smem = NSTAGE * sizeof(Stage);
-  st = allow_lds((const void*)attn_fwd<WITH_O, kHalvesPerWave>, smem, "attention");
+  sx_status st = allow_lds((const void*)attn_fwd<WITH_O, kHalvesPerWave>, smem, "attention");
   if (st != SX_OK) return st;
   const float scale_log2 = kLog2e / sqrtf((float)dims.head_dim);
   attn_fwd<WITH_O, kHalvesPerWave><<<L.max_items * hkv, 64 * (8 / kHalvesPerWave), smem, stream>>>(
@@ -943,10 +954,27 @@ sx_status launch_bf16(const sx_dims& dims, const sx_layout& lay, const void* q,
       L.max_items, scale_log2);
   st = check_launch("attention");
   if (st != SX_OK) return st;
-  if (!may_split) return SX_OK;
+  if (!attn_may_split(n_rows, G, hkv)) return SX_OK;
   attn_merge<WITH_O><<<L.max_tiles * hkv * (PAIRS / kMergePairs), 256, 0, stream>>>(merges, counters, hkv, G, part_ml,
                                                            part_o, (uint16_t*)o, lse, L.max_items);
   return check_launch("attention merge");
+}
+
+sx_status run_f32(const sx_dims& dims, const sx_layout& lay, const void* q, const int32_t* q_index,
+                  const int32_t* rows, int n_rows, const sx_pages& kv, void* o, float* lse,
+                  hipStream_t stream) {
+  const int hq = dims.n_q_heads, hkv = dims.n_kv_heads, d = dims.head_dim;
+  const float scale = 1.f / sqrtf((float)d);
+  dim3 grid(n_rows, hq);
+  if (d == 64)
+    attn_rows_f32<64><<<grid, 64, 0, stream>>>((const float*)q, q_index, rows, n_rows, lay,
+                                               kv.n_pages, (const float*)kv.k, (const float*)kv.v,
+                                               hkv, hq, (float*)o, lse, scale);
+  else
+    attn_rows_f32<128><<<grid, 64, 0, stream>>>((const float*)q, q_index, rows, n_rows, lay,
+                                                kv.n_pages, (const float*)kv.k, (const float*)kv.v,
+                                                hkv, hq, (float*)o, lse, scale);
+  return check_launch("attention (fp32)");
 }
 
 }  // namespace
@@ -957,27 +985,29 @@ size_t attn_ws_bytes(const sx_dims& dims, int n_rows, int n_req, bool with_o) {
   return ws_layout(n_rows, n_req, G, dims.n_kv_heads, with_o).total;
 }
 
+sx_status launch_attention_plan(const sx_dims& dims, const sx_layout& lay, const int32_t* rows,
+                                const int32_t* row_start, int n_rows, void* ws, hipStream_t stream) {
+  if (n_rows == 0 || dims.dtype != SX_BF16) return SX_OK;   // fp32 rows need no work list
+  return plan_bf16(dims, lay, rows, row_start, n_rows, ws, stream);
+}
+
+sx_status launch_attention_run(const sx_dims& dims, const sx_layout& lay, const void* q,
+                               const int32_t* q_index, const int32_t* rows, int n_rows,
+                               const sx_pages& kv, void* o, float* lse, void* ws,
+                               hipStream_t stream) {
+  if (n_rows == 0) return SX_OK;
+  if (dims.dtype != SX_BF16) return run_f32(dims, lay, q, q_index, rows, n_rows, kv, o, lse, stream);
+  return o ? run_bf16<true>(dims, lay, q, q_index, rows, n_rows, kv, o, lse, ws, stream)
+           : run_bf16<false>(dims, lay, q, q_index, rows, n_rows, kv, o, lse, ws, stream);
+}
+
 sx_status launch_attention(const sx_dims& dims, const sx_layout& lay, const void* q,
                            const int32_t* q_index, const int32_t* rows,
                            const int32_t* row_start, int n_rows, const sx_pages& kv, void* o,
                            float* lse, void* ws, hipStream_t stream) {
-  if (n_rows == 0) return SX_OK;
-  const int hq = dims.n_q_heads, hkv = dims.n_kv_heads, d = dims.head_dim;
-  if (dims.dtype != SX_BF16) {
-    const float scale = 1.f / sqrtf((float)d);
-    dim3 grid(n_rows, hq);
-    if (d == 64)
-      attn_rows_f32<64><<<grid, 64, 0, stream>>>((const float*)q, q_index, rows, n_rows, lay,
-                                                 kv.n_pages, (const float*)kv.k, (const float*)kv.v,
-                                                 hkv, hq, (float*)o, lse, scale);
-    else
-      attn_rows_f32<128><<<grid, 64, 0, stream>>>((const float*)q, q_index, rows, n_rows, lay,
-                                                  kv.n_pages, (const float*)kv.k, (const float*)kv.v,
-                                                  hkv, hq, (float*)o, lse, scale);
-    return check_launch("attention (fp32)");
-  }
-  return o ? launch_bf16<true>(dims, lay, q, q_index, rows, row_start, n_rows, kv, o, lse, ws, stream)
-           : launch_bf16<false>(dims, lay, q, q_index, rows, row_start, n_rows, kv, o, lse, ws, stream);
+  const sx_status st = launch_attention_plan(dims, lay, rows, row_start, n_rows, ws, stream);
+  if (st != SX_OK) return st;
+  return launch_attention_run(dims, lay, q, q_index, rows, n_rows, kv, o, lse, ws, stream);
 }
 
 }  // namespace sx

@@ -43,6 +43,16 @@ sx_status launch_attention(const sx_dims& dims, const sx_layout& lay, const void
                            const int32_t* row_start, int n_rows, const sx_pages& kv, void* o,
                            float* lse, void* ws, hipStream_t stream);
 
+// The two halves of launch_attention: the work list over the rows (into ws;
+// a no-op for fp32) and the attention over a work list already in ws, built
+// for the same rows, layout and dims.
+sx_status launch_attention_plan(const sx_dims& dims, const sx_layout& lay, const int32_t* rows,
+                                const int32_t* row_start, int n_rows, void* ws, hipStream_t stream);
+sx_status launch_attention_run(const sx_dims& dims, const sx_layout& lay, const void* q,
+                               const int32_t* q_index, const int32_t* rows, int n_rows,
+                               const sx_pages& kv, void* o, float* lse, void* ws,
+                               hipStream_t stream);
+
 // Decode attention: one query row per request (its last token), bf16 only.
 size_t decode_ws_bytes(const sx_dims& d, int n_tok, int n_req);
 sx_status launch_decode(const sx_dims& dims, const sx_layout& lay, const void* q, const sx_pages& kv,

@@ -186,11 +186,18 @@ class HybridStackRun:
             L.sx_recompute_kv(self.cdims, self.lay.struct, x, self.act_rows, self.n_act, w, pages,
                               self.q_act_buf[l % 2])
 
+    def attn_plan(self, timer=None):
+        """The active set is fixed once the selection is made (§3.4): the
+        attention's work list over it is built once for every sparse layer."""
+        with _phase(timer, "attn_plan"):
+            L.sx_sparse_attn_plan(self.cdims, self.lay.struct, self.act_rows, self.act_start, self.n_act,
+                                  self.ws_attn)
+
     def sparse_attn(self, l: int, timer=None):
         with _phase(timer, "sparse_attn"):
-            L.sx_sparse_attn(self.cdims, self.lay.struct, self.q_act_buf[l % 2], self.act_rows,
-                             self.act_start, self.n_act, self.req_pools[l].struct(), self.o_act[l], None,
-                             self.ws_attn)
+            L.sx_sparse_attn_run(self.cdims, self.lay.struct, self.q_act_buf[l % 2], self.act_rows,
+                                 self.n_act, self.req_pools[l].struct(), self.o_act[l], None,
+                                 self.ws_attn)
 
     def sparse_layer(self, l: int, timer=None, realign: bool = True):
         self.sparse_prep(l, timer, realign)
@@ -266,6 +273,7 @@ class HybridStackRun:
         mark("sparse")
         if self.t > 0:
             self.select(self.t - 1, timer)
+            self.attn_plan(timer)
             if pipelined:
                 self.sparse_layers_pipelined(self.t, timer)
             else:
@@ -273,6 +281,7 @@ class HybridStackRun:
                     self.sparse_layer(l, timer)
         else:
             self.select_in_layer(0, timer)
+            self.attn_plan(timer)
             if pipelined:
                 self.sparse_layers_pipelined(0, timer, first_realigned=True)
             else:

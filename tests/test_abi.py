@@ -80,6 +80,15 @@ def test_validation_errors_launch_nothing():
     assert lib.sx_recompute_kv(C.byref(d), C.byref(bad_lay), FAKE, FAKE, 1, FAKE, C.byref(pages), None,
                                None) == L.SX_EINVAL
     assert lib.sx_topk(None, FAKE, FAKE, 1, 4, FAKE, FAKE, None, 0, None) == L.SX_EINVAL
+    # plan / run halves of the sparse attention
+    assert lib.sx_sparse_attn_plan(C.byref(d), C.byref(lay), None, FAKE, 4, FAKE, 1 << 20, None) == L.SX_EINVAL
+    assert lib.sx_sparse_attn_plan(C.byref(d), C.byref(lay), FAKE, FAKE, 100, FAKE, 8, None) == L.SX_EWORKSPACE
+    assert lib.sx_sparse_attn_run(C.byref(d), C.byref(lay), FAKE, FAKE, 100, C.byref(pages), FAKE, None,
+                                  FAKE, 8, None) == L.SX_EWORKSPACE
+    assert lib.sx_sparse_attn_run(C.byref(d), C.byref(lay), None, FAKE, 4, C.byref(pages), FAKE, None,
+                                  FAKE, 1 << 20, None) == L.SX_EINVAL
+    assert lib.sx_sparse_attn_run(C.byref(d), C.byref(lay), FAKE, FAKE, -1, C.byref(pages), FAKE, None,
+                                  FAKE, 1 << 20, None) == L.SX_EINVAL
     # MFMA probe: sizes and output are checked before any launch
     assert lib.sx_mfma_peak_probe(0, 10, FAKE, None) == L.SX_EINVAL
     assert lib.sx_mfma_peak_probe(4, 0, FAKE, None) == L.SX_EINVAL
@@ -96,6 +105,9 @@ def test_zero_sized_calls_are_noops():
     assert lib.sx_sparse_attn(C.byref(d), C.byref(lay), None, None, None, 0, C.byref(pages), None, None,
                               None, 0, None) == 0
     assert lib.sx_rope_realign(C.byref(d), C.byref(lay), C.byref(pages), C.byref(pages), None, 0, None) == 0
+    assert lib.sx_sparse_attn_plan(C.byref(d), C.byref(lay), None, None, 0, None, 0, None) == 0
+    assert lib.sx_sparse_attn_run(C.byref(d), C.byref(lay), None, None, 0, C.byref(pages), None, None,
+                                  None, 0, None) == 0
 
 
 def test_workspace_sizes_are_monotone():

@@ -243,6 +243,47 @@ def test_sparse_attention_parity(shape, lens, density, qscale):
             assert np.max(np.abs(lg[sl] - lref)) < 1e-4
 
 
+@pytest.mark.parametrize("shape,lens,density", [("llama", [700, 333], 0.3), ("llama", [3000, 1200], 0.9),
+                                                ("tiny", [144, 50], 0.5)])
+def test_sparse_attention_plan_then_runs_equal_one_shot(shape, lens, density):
+    """sx_sparse_attn_plan once, then sx_sparse_attn_run for two different
+    query sets: bit-identical to sx_sparse_attn on each.  The first case has
+    few rows (tiles split into key chunks, merge pass), the second enough
+    rows that nothing is split, the third is the fp32 path (no work list)."""
+    dims = SHAPES[shape]
+    say(f"[attn plan/run] shape={shape} lens={lens} density={density}")
+    rng, seq, pool, kh, vh, bt = _attn_inputs(dims, lens, 37)
+    rows, starts = [], [0]
+    for r, n in enumerate(lens):
+        sel = np.union1d(np.flatnonzero(rng.random(n) < density), [0, n - 1])
+        rows.append(sel + seq[r])
+        starts.append(starts[-1] + len(sel))
+    rows = np.concatenate(rows).astype(np.int32)
+    n_rows = len(rows)
+    dt = LY.storage_dtype(dims.dtype)
+    rope = LY.rope_table(dims.theta, dims.head_dim, 16, DEV)
+    lay = LY.DeviceLayout(seq, bt, rope, DEV)
+    cd = LY.make_dims(dims)
+    rd = torch.from_numpy(rows).to(DEV)
+    sd = torch.from_numpy(np.array(starts, np.int32)).to(DEV)
+    qs = [torch.from_numpy(_store(rng.standard_normal((n_rows, dims.n_q_heads, dims.head_dim)), dims)).to(dt).to(DEV)
+          for _ in range(2)]
+    ws = LY.workspace(L.SX_OP_SPARSE_ATTN, cd, int(seq[-1]), n_rows, len(lens), DEV)
+    ws2 = LY.workspace(L.SX_OP_SPARSE_ATTN, cd, int(seq[-1]), n_rows, len(lens), DEV)
+    L.sx_sparse_attn_plan(cd, lay.struct, rd, sd, n_rows, ws2)
+    for q in qs:
+        o1 = torch.zeros((n_rows, dims.n_q_heads * dims.head_dim), dtype=dt, device=DEV)
+        o2 = torch.full_like(o1, 7.0)
+        l1 = torch.zeros((n_rows, dims.n_q_heads), dtype=torch.float32, device=DEV)
+        l2 = torch.full_like(l1, 7.0)
+        L.sx_sparse_attn(cd, lay.struct, q, rd, sd, n_rows, pool.struct(), o1, l1, ws)
+        L.sx_sparse_attn_run(cd, lay.struct, q, rd, n_rows, pool.struct(), o2, l2, ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16) if dt != torch.float32 else o1.view(torch.int32),
+                           o2.view(torch.int16) if dt != torch.float32 else o2.view(torch.int32))
+        assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
 @pytest.mark.parametrize("shape,lens", [("llama", [900, 130]), ("tiny", [144])])
 def test_full_attention_parity(shape, lens):
     dims = SHAPES[shape]
