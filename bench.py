@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "prefill tokens/s per layer @32K (sparse recompute); attn % of MFMA bf16 peak"
+METRIC_QWEN = "prefill tokens/s per layer @128K (sparse recompute); attn % of MFMA bf16 peak"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_rag32k_traffic.json")
@@ -47,8 +48,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--threshold", type=int, default=4)
+    ap.add_argument("--workload", choices=["rag32k", "qwen128k"], default="rag32k",
+                    help="rag32k (the metric's workload, default) or qwen128k: Qwen2.5-7B shapes, "
+                         "32 reused 4,000-token segments + 1,024 new tokens, 28 layers, threshold 8")
+    ap.add_argument("--layers", type=int, default=None, help="default 32 (rag32k) / 28 (qwen128k)")
+    ap.add_argument("--threshold", type=int, default=None, help="default 4 (rag32k) / 8 (qwen128k)")
     ap.add_argument("--pipelined", action="store_true",
                     help="run the sparse layers on two streams (layer l+1's realign and recompute "
                          "while layer l attends)")
@@ -275,15 +279,29 @@ def main():
     from segment_level_kv_amd import synth
     from segment_level_kv_amd.stack import HybridStackRun, phase_counts, phase_ms
 
-    dims = synth.LLAMA8B
-    seg_lengths, layout, p_src = synth.rag_layout()
+    qwen = args.workload == "qwen128k"
+    if qwen:
+        # the 32 segments were cached together in a first request, in a seeded
+        # order; the measured request reuses them in index order + 1,024 new
+        dims = synth.QWEN7B
+        seg_lengths, layout = synth.qwen_layout()
+        order = np.random.default_rng(1005).permutation(len(seg_lengths))
+        p_src = [int(order[i]) * seg_lengths[i] for i in range(len(seg_lengths))]
+        n_layers = args.layers if args.layers is not None else 28
+        t = args.threshold if args.threshold is not None else 8
+        seed = 1005
+    else:
+        dims = synth.LLAMA8B
+        seg_lengths, layout, p_src = synth.rag_layout()
+        n_layers = args.layers if args.layers is not None else 32
+        t = args.threshold if args.threshold is not None else 4
+        seed = 1003
     seg_len = {i: n for i, n in enumerate(seg_lengths)}
     seg_p = {i: p for i, p in enumerate(p_src)}
-    n_layers, t = args.layers, args.threshold
-    n_tok = sum(seg_lengths) + 256
+    n_tok = sum(seg_len[v] if k == "reuse" else v for k, v in layout)
     n_cache = sum(seg_lengths)
     dev = "cuda"
-    inputs = synth.TorchStackInputs(1003, dims, n_layers, n_tok, n_cache, t, dev)
+    inputs = synth.TorchStackInputs(seed, dims, n_layers, n_tok, n_cache, t, dev)
     run = HybridStackRun(dims, n_layers, t, [layout], seg_len, seg_p, [(10, 100)], inputs, dev)
     run.build_caches()
     torch.cuda.synchronize()
@@ -331,7 +349,8 @@ def main():
     flops = 4.0 * dims.head_dim * dims.n_q_heads * float(np.sum(pos + 1))
     attn_ms = ph["sparse_attn"] / cnt["sparse_attn"]
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    traffic = measured_traffic()
+    # the committed counters are of the rag32k workload
+    traffic = None if qwen else measured_traffic()
     # other phases (per launch)
     reused = sum(seg_lengths)
     realign_bytes = 2.0 * reused * dims.n_kv_heads * dims.head_dim * 2 * 2   # K+V read + write
@@ -345,7 +364,7 @@ def main():
     plan_ms = ph.get("attn_plan", 0) / max(cnt.get("attn_plan", 1), 1)
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_QWEN if qwen else METRIC,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -358,7 +377,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": ("rag32k: 32-layer Llama-3-8B-shaped attention stack (hidden 4096, 32/8 heads, "
+            "workload": (f"qwen128k: {n_layers}-layer Qwen2.5-7B-shaped attention stack (hidden 3584, "
+                         "28/4 heads, head_dim 128), 32 reused 4000-token segments (cached together in a "
+                         f"seeded order) + 1024 new = {T} tokens, full layers 0-{t - 1}, sparse "
+                         f"{t}-{n_layers - 1}, ratio 10%") if qwen else
+                        ("rag32k: 32-layer Llama-3-8B-shaped attention stack (hidden 4096, 32/8 heads, "
                          "head_dim 128), 512 reused system + 16x1920 reused passages + 256 new "
                          f"= {T} tokens, full layers 0-{t - 1}, sparse {t}-{n_layers - 1}, ratio 10%"),
             "tokens": T, "active_rows": int(run.n_act), "selected": int(run.n_sel),
@@ -420,7 +443,7 @@ def main():
     peak = mfma_peak_measure()
     out["mfma_peak_measured"] = peak
     out["attn_pct_measured_mfma_peak"] = round(100.0 * achieved / peak["TFLOP/s"], 2)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not qwen:
         out["cpu_baseline"] = cpu_baseline(dims, run.plan, n_sparse, T, reused)
     print(json.dumps(out), flush=True)
 
