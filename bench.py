@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "prefill tokens/s per layer @32K (sparse recompute); attn % of MFMA bf16 peak"
 METRIC_QWEN = "prefill tokens/s per layer @128K (sparse recompute); attn % of MFMA bf16 peak"
+METRIC_AGENT = "prefill tokens/s, one layer, 4 x ~64K agent batch (sparse recompute); attn % of MFMA bf16 peak"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_rag32k_traffic.json")
@@ -48,9 +49,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["rag32k", "qwen128k"], default="rag32k",
-                    help="rag32k (the metric's workload, default) or qwen128k: Qwen2.5-7B shapes, "
-                         "32 reused 4,000-token segments + 1,024 new tokens, 28 layers, threshold 8")
+    ap.add_argument("--workload", choices=["rag32k", "qwen128k", "agent64k"], default="rag32k",
+                    help="rag32k (the metric's workload, default); qwen128k: Qwen2.5-7B shapes, "
+                         "32 reused 4,000-token segments + 1,024 new tokens, 28 layers, threshold 8; "
+                         "agent64k: Llama shapes, 4 requests of ~64K tokens from a pool of 64 "
+                         "segments, ratios 5-30%, one layer (selection inside it)")
     ap.add_argument("--layers", type=int, default=None, help="default 32 (rag32k) / 28 (qwen128k)")
     ap.add_argument("--threshold", type=int, default=None, help="default 4 (rag32k) / 8 (qwen128k)")
     ap.add_argument("--pipelined", action="store_true",
@@ -95,8 +98,9 @@ def decode_measure(run, dims, n_layers: int, t: int, reps: int = 5):
     hq, hkv, d = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
     g = torch.Generator(device="cuda")
     g.manual_seed(99)
-    q = torch.randn((1, hq, d), generator=g, device="cuda").to(torch.bfloat16)
-    o = torch.empty((1, hq * d), dtype=torch.bfloat16, device="cuda")
+    n_req = run.n_req
+    q = torch.randn((n_req, hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    o = torch.empty((n_req, hq * d), dtype=torch.bfloat16, device="cuda")
     layers = list(range(t, n_layers))
     for l in layers:
         run.decode_attention(l, q, o)
@@ -110,7 +114,7 @@ def decode_measure(run, dims, n_layers: int, t: int, reps: int = 5):
     b.record()
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / (reps * len(layers))
-    nbytes = 2.0 * T * hkv * d * 2 + 2.0 * 2 * hq * d
+    nbytes = 2.0 * T * hkv * d * 2 + 2.0 * 2 * n_req * hq * d
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"kernel": "sx_decode_attn (decode_fwd + decode_merge)", "tokens": T,
             "us_per_call": round(us, 2), "bytes_per_call": nbytes, "achieved_GBps": round(gbs, 1),
@@ -280,7 +284,18 @@ def main():
     from segment_level_kv_amd.stack import HybridStackRun, phase_counts, phase_ms
 
     qwen = args.workload == "qwen128k"
-    if qwen:
+    agent = args.workload == "agent64k"
+    ratios = None
+    if agent:
+        # each pool segment cached alone at an offset in [0, 8192 - L]
+        dims = synth.LLAMA8B
+        seg_lengths, layouts, ratios = synth.agent_layout()
+        rng = np.random.default_rng(1021)
+        p_src = [int(rng.integers(0, 8192 - n + 1)) for n in seg_lengths]
+        n_layers = args.layers if args.layers is not None else 1
+        t = args.threshold if args.threshold is not None else 0
+        seed = 1004
+    elif qwen:
         # the 32 segments were cached together in a first request, in a seeded
         # order; the measured request reuses them in index order + 1,024 new
         dims = synth.QWEN7B
@@ -296,13 +311,15 @@ def main():
         n_layers = args.layers if args.layers is not None else 32
         t = args.threshold if args.threshold is not None else 4
         seed = 1003
+    if not agent:
+        layouts, ratios = [layout], [(10, 100)]
     seg_len = {i: n for i, n in enumerate(seg_lengths)}
     seg_p = {i: p for i, p in enumerate(p_src)}
-    n_tok = sum(seg_len[v] if k == "reuse" else v for k, v in layout)
+    n_tok = sum(seg_len[v] if k == "reuse" else v for lay in layouts for k, v in lay)
     n_cache = sum(seg_lengths)
     dev = "cuda"
     inputs = synth.TorchStackInputs(seed, dims, n_layers, n_tok, n_cache, t, dev)
-    run = HybridStackRun(dims, n_layers, t, [layout], seg_len, seg_p, [(10, 100)], inputs, dev)
+    run = HybridStackRun(dims, n_layers, t, layouts, seg_len, seg_p, ratios, inputs, dev)
     run.build_caches()
     torch.cuda.synchronize()
     if args.calib_copy_mib > 0:
@@ -345,14 +362,15 @@ def main():
 
     # sparse attention roofline: unmasked MACs of QK^T and PV
     act = run.act_rows[:run.n_act].cpu().numpy().astype(np.int64)
-    pos = act - run.seq_start_h[0]
+    seq_h = np.asarray(run.seq_start_h, dtype=np.int64)
+    pos = act - seq_h[np.searchsorted(seq_h, act, side="right") - 1]     # index in its request
     flops = 4.0 * dims.head_dim * dims.n_q_heads * float(np.sum(pos + 1))
     attn_ms = ph["sparse_attn"] / cnt["sparse_attn"]
     achieved = flops / (attn_ms * 1e-3) / 1e12
     # the committed counters are of the rag32k workload
-    traffic = None if qwen else measured_traffic()
+    traffic = None if (qwen or agent) else measured_traffic()
     # other phases (per launch)
-    reused = sum(seg_lengths)
+    reused = sum(seg_len[v] for lay in layouts for k, v in lay if k == "reuse")
     realign_bytes = 2.0 * reused * dims.n_kv_heads * dims.head_dim * 2 * 2   # K+V read + write
     realign_ms = ph["realign"] / cnt["realign"]
     rec_flops = 2.0 * run.n_act * dims.qkv_rows * dims.hidden
@@ -364,7 +382,7 @@ def main():
     plan_ms = ph.get("attn_plan", 0) / max(cnt.get("attn_plan", 1), 1)
 
     out = {
-        "metric": METRIC_QWEN if qwen else METRIC,
+        "metric": METRIC_QWEN if qwen else (METRIC_AGENT if agent else METRIC),
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -377,7 +395,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": (f"qwen128k: {n_layers}-layer Qwen2.5-7B-shaped attention stack (hidden 3584, "
+            "workload": (f"agent64k: {n_layers}-layer Llama-3-8B-shaped attention stack, {len(layouts)} "
+                         f"requests ({T} tokens) drawn from a pool of 64 reused segments of 32-2048 tokens, "
+                         "no new tokens (tail fallback), ratios 5-30% per request, selection inside "
+                         "layer 0") if agent else
+                        (f"qwen128k: {n_layers}-layer Qwen2.5-7B-shaped attention stack (hidden 3584, "
                          "28/4 heads, head_dim 128), 32 reused 4000-token segments (cached together in a "
                          f"seeded order) + 1024 new = {T} tokens, full layers 0-{t - 1}, sparse "
                          f"{t}-{n_layers - 1}, ratio 10%") if qwen else
@@ -418,7 +440,8 @@ def main():
     # every kernel of the sparse layer (and the full layer) against its roofline,
     # per launch; the selection's work is the QK^T of the Sparse-Q rows over
     # their key prefixes, once for the LSE probe and once for the scores
-    sq = np.asarray(run.plan["sq_rows"], dtype=np.int64) - int(run.seq_start_h[0])
+    sq_tok = np.asarray(run.plan["sq_rows"], dtype=np.int64)
+    sq = sq_tok - seq_h[np.searchsorted(seq_h, sq_tok, side="right") - 1]
     sel_flops = 2 * (2.0 * dims.head_dim * dims.n_q_heads * float(np.sum(sq + 1)))
     full_rec_flops = 2.0 * T * dims.qkv_rows * dims.hidden
     rate = lambda work, ms, unit: round(work / (ms * 1e-3) / unit, 1) if ms else None
@@ -443,7 +466,7 @@ def main():
     peak = mfma_peak_measure()
     out["mfma_peak_measured"] = peak
     out["attn_pct_measured_mfma_peak"] = round(100.0 * achieved / peak["TFLOP/s"], 2)
-    if not args.no_cpu_baseline and not qwen:
+    if not args.no_cpu_baseline and not (qwen or agent):
         out["cpu_baseline"] = cpu_baseline(dims, run.plan, n_sparse, T, reused)
     print(json.dumps(out), flush=True)
 
