@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "prefill tokens/s per layer @32K (sparse recompute); attn % of MFMA bf16 peak"
 METRIC_QWEN = "prefill tokens/s per layer @128K (sparse recompute); attn % of MFMA bf16 peak"
+METRIC_1L = "prefill tokens/s, one Llama-3-8B-shaped layer at 4.3K (sparse recompute); attn % of MFMA bf16 peak"
 METRIC_AGENT = "prefill tokens/s, one layer, 4 x ~64K agent batch (sparse recompute); attn % of MFMA bf16 peak"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
@@ -49,11 +50,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["rag32k", "qwen128k", "agent64k"], default="rag32k",
+    ap.add_argument("--workload", choices=["rag32k", "qwen128k", "agent64k", "llama1l"], default="rag32k",
                     help="rag32k (the metric's workload, default); qwen128k: Qwen2.5-7B shapes, "
                          "32 reused 4,000-token segments + 1,024 new tokens, 28 layers, threshold 8; "
                          "agent64k: Llama shapes, 4 requests of ~64K tokens from a pool of 64 "
-                         "segments, ratios 5-30%, one layer (selection inside it)")
+                         "segments, ratios 5-30%, one layer (selection inside it); llama1l: 8 x 512 "
+                         "reused + 256 new tokens, ratio 15%, one layer")
     ap.add_argument("--layers", type=int, default=None, help="default 32 (rag32k) / 28 (qwen128k)")
     ap.add_argument("--threshold", type=int, default=None, help="default 4 (rag32k) / 8 (qwen128k)")
     ap.add_argument("--pipelined", action="store_true",
@@ -285,8 +287,20 @@ def main():
 
     qwen = args.workload == "qwen128k"
     agent = args.workload == "agent64k"
+    llama1l = args.workload == "llama1l"
     ratios = None
-    if agent:
+    if llama1l:
+        # each segment cached alone at an offset in [0, 8192 - 512]
+        dims = synth.LLAMA8B
+        seg_lengths = [512] * 8
+        layouts = [[("reuse", i) for i in range(8)] + [("new", 256)]]
+        ratios = [(15, 100)]
+        rng = np.random.default_rng(1022)
+        p_src = [int(rng.integers(0, 8192 - 512 + 1)) for _ in seg_lengths]
+        n_layers = args.layers if args.layers is not None else 1
+        t = args.threshold if args.threshold is not None else 0
+        seed = 1002
+    elif agent:
         # each pool segment cached alone at an offset in [0, 8192 - L]
         dims = synth.LLAMA8B
         seg_lengths, layouts, ratios = synth.agent_layout()
@@ -311,7 +325,7 @@ def main():
         n_layers = args.layers if args.layers is not None else 32
         t = args.threshold if args.threshold is not None else 4
         seed = 1003
-    if not agent:
+    if not (agent or llama1l):
         layouts, ratios = [layout], [(10, 100)]
     seg_len = {i: n for i, n in enumerate(seg_lengths)}
     seg_p = {i: p for i, p in enumerate(p_src)}
@@ -368,7 +382,7 @@ def main():
     attn_ms = ph["sparse_attn"] / cnt["sparse_attn"]
     achieved = flops / (attn_ms * 1e-3) / 1e12
     # the committed counters are of the rag32k workload
-    traffic = None if (qwen or agent) else measured_traffic()
+    traffic = None if (qwen or agent or llama1l) else measured_traffic()
     # other phases (per launch)
     reused = sum(seg_len[v] for lay in layouts for k, v in lay if k == "reuse")
     realign_bytes = 2.0 * reused * dims.n_kv_heads * dims.head_dim * 2 * 2   # K+V read + write
@@ -382,7 +396,7 @@ def main():
     plan_ms = ph.get("attn_plan", 0) / max(cnt.get("attn_plan", 1), 1)
 
     out = {
-        "metric": METRIC_QWEN if qwen else (METRIC_AGENT if agent else METRIC),
+        "metric": METRIC_QWEN if qwen else (METRIC_AGENT if agent else (METRIC_1L if llama1l else METRIC)),
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -395,7 +409,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": (f"agent64k: {n_layers}-layer Llama-3-8B-shaped attention stack, {len(layouts)} "
+            "workload": (f"llama1l: {n_layers}-layer Llama-3-8B-shaped attention stack, 8 reused 512-token "
+                         f"segments (each cached alone at an offset in [0, 7680]) + 256 new = {T} tokens, "
+                         "ratio 15%, selection inside layer 0") if llama1l else
+                        (f"agent64k: {n_layers}-layer Llama-3-8B-shaped attention stack, {len(layouts)} "
                          f"requests ({T} tokens) drawn from a pool of 64 reused segments of 32-2048 tokens, "
                          "no new tokens (tail fallback), ratios 5-30% per request, selection inside "
                          "layer 0") if agent else
@@ -466,7 +483,7 @@ def main():
     peak = mfma_peak_measure()
     out["mfma_peak_measured"] = peak
     out["attn_pct_measured_mfma_peak"] = round(100.0 * achieved / peak["TFLOP/s"], 2)
-    if not args.no_cpu_baseline and not (qwen or agent):
+    if not args.no_cpu_baseline and not (qwen or agent or llama1l):
         out["cpu_baseline"] = cpu_baseline(dims, run.plan, n_sparse, T, reused)
     print(json.dumps(out), flush=True)
 
