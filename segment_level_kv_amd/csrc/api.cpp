@@ -407,7 +407,7 @@ sx_status sx_select_topk(const sx_dims* dims, const sx_layout* lay, const void* 
   hipStream_t s = as_stream(stream);
   char* p = static_cast<char*>(ws);
   float* partial = reinterpret_cast<float*>(p);
-  p += align256((size_t)dims->n_kv_heads * lay->n_tok * sizeof(float));
+  p += align256((size_t)score_parts(*dims, lay->n_tok, lay->n_req) * lay->n_tok * sizeof(float));
   float* score_buf = reinterpret_cast<float*>(p);
   p += align256((size_t)lay->n_tok * sizeof(float));
   float* lse_buf = reinterpret_cast<float*>(p);
@@ -427,7 +427,7 @@ sx_status sx_select_topk(const sx_dims* dims, const sx_layout* lay, const void* 
     SX_TRY(launch_scores(*dims, *lay, q, q_index, sq_rows, sq_start, n_sq, lse_use, lse_index, *kv,
                          partial, s));
   }
-  return launch_topk(partial, dims->n_kv_heads, tok_class, lay->seq_start, lay->n_req, lay->n_tok,
+  return launch_topk(partial, score_parts(*dims, lay->n_tok, lay->n_req), tok_class, lay->seq_start, lay->n_req, lay->n_tok,
                      k_sel, sq_start, sel_rows, act_rows, scores ? scores : score_buf, nullptr, s);
 }
 

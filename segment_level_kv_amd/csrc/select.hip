@@ -5,13 +5,16 @@
 //
 //   score[j] = sum_h sum_{i in I_nr, i >= j} exp(q_i^h . k_j / sqrt(d) - lse_i^h)
 //
-// Score pass (bf16): one workgroup per (256-key tile of a request, kv head);
-// each wave keeps the K operand of its 64 keys in registers, the Sparse-Q
-// rows of one query head stream through LDS 32 at a time, S = Q . K^T runs
-// on v_mfma_f32_32x32x16_bf16 with the key axis across lanes, and each lane
-// sums exp(S - lse) over the queries in registers.  Partial sums per kv head
-// go to a [Hkv][n_tok] buffer; the top-k kernel adds them in head order, so
-// every score is the same fixed-order fp32 sum run to run.
+// Score pass (bf16): one workgroup per (256-key tile of a request, kv head)
+// taking the G query heads of the group in turn, or, when that grid would
+// leave compute units idle (short prompts), per (tile, query head); each
+// wave keeps the K operand of its 64 keys in registers, the Sparse-Q rows of
+// one query head stream through LDS 32 at a time, S = Q . K^T runs on
+// v_mfma_f32_32x32x16_bf16 with the key axis across lanes, and each lane
+// sums exp(S - lse) over the queries in registers.  Partial sums per
+// workgroup row go to a [parts][n_tok] buffer (parts = Hkv or Hq); the top-k
+// kernel adds them in row order, so every score is the same fixed-order fp32
+// sum run to run.
 //
 // Top-k: one workgroup per request.  Order-preserving 32-bit keys of the
 // scores (-0 mapped to +0), a 4-pass 8-bit radix select for the k-th largest
@@ -58,12 +61,13 @@ __global__ __launch_bounds__(256) void scores_bf16(
     const int32_t* __restrict__ sq_rows, const int32_t* __restrict__ sq_start,
     const float* __restrict__ lse, const int32_t* __restrict__ lse_index, sx_layout lay,
     int n_pages, const uint16_t* __restrict__ kpool, int hq, int hkv,
-    float* __restrict__ partial, float scale_log2) {
+    float* __restrict__ partial, float scale_log2, int hpw) {
   __shared__ ScoreSmem sm;
   int req, k0;
   if (!score_tile(lay.seq_start, lay.n_req, blockIdx.x, req, k0)) return;
-  const int g = blockIdx.y;
   const int G = hq / hkv;
+  const int h0 = blockIdx.y * hpw;            // the hpw query heads of this workgroup
+  const int g = h0 / G;                       // their kv head
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hl = lane >> 5;
   const int seq0 = lay.seq_start[req];
   const int len = lay.seq_start[req + 1] - seq0;
@@ -98,13 +102,13 @@ __global__ __launch_bounds__(256) void scores_bf16(
   int bfirst = s0;
   while (bfirst < s1 && sq_rows[min(bfirst + SQB, s1) - 1] - seq0 < k0) bfirst += SQB;
   const int n_blk = (s1 - bfirst + SQB - 1) / SQB;
-  const int n_it = n_blk * G;                // iteration it: head it / n_blk, block it % n_blk
+  const int n_it = n_blk * hpw;              // iteration it: head h0 + it / n_blk, block it % n_blk
   constexpr int QU = SQB * 16 / 256;         // 16-byte Q chunks per thread and block
   u32x4 qn[QU];
   float lse_n = INFINITY;
   int pos_n = -1;
   auto fetch = [&](int it) __attribute__((always_inline)) {
-    const int h = g * G + it / n_blk;
+    const int h = h0 + it / n_blk;
     const int b0 = bfirst + (it % n_blk) * SQB;
 #pragma unroll
     for (int e = 0; e < QU; ++e) {
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(256) void scores_bf16(
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const float tot = acc[nb] + __shfl_xor(acc[nb], 32);
-    if (hl == 0 && key_idx[nb] < len) partial[(size_t)g * lay.n_tok + seq0 + key_idx[nb]] = tot;
+    if (hl == 0 && key_idx[nb] < len) partial[(size_t)blockIdx.y * lay.n_tok + seq0 + key_idx[nb]] = tot;
   }
 }
 
@@ -407,10 +411,20 @@ size_t topk_ws_bytes(int n_tok, int n_req) {
 }
 
 size_t select_ws_bytes(const sx_dims& d, int n_tok, int n_sq, int n_req) {
-  return align256((size_t)d.n_kv_heads * n_tok * sizeof(float))   // partial scores
+  return align256((size_t)score_parts(d, n_tok, n_req) * n_tok * sizeof(float))  // partial scores
          + align256((size_t)n_tok * sizeof(float))                // scores if caller passes none
          + align256((size_t)n_sq * d.n_q_heads * sizeof(float))   // probe LSE
          + attn_ws_bytes(d, n_sq, n_req, false);                   // probe work list
+}
+
+// Key tiles of the score grid (>= the sum of the per-request tile counts).
+int score_tiles(int n_tok, int n_req) { return n_tok / SKT + n_req + 1; }
+
+// bf16: a workgroup takes the G query heads of one kv head, unless that grid
+// would leave compute units idle (short prompts); then one query head each.
+int score_parts(const sx_dims& d, int n_tok, int n_req) {
+  if (d.dtype != SX_BF16) return d.n_kv_heads;
+  return (long long)score_tiles(n_tok, n_req) * d.n_kv_heads < 512 ? d.n_q_heads : d.n_kv_heads;
 }
 
 sx_status launch_scores(const sx_dims& dims, const sx_layout& lay, const void* q,
@@ -420,10 +434,10 @@ sx_status launch_scores(const sx_dims& dims, const sx_layout& lay, const void* q
   (void)n_sq;
   const int hq = dims.n_q_heads, hkv = dims.n_kv_heads, d = dims.head_dim;
   if (dims.dtype == SX_BF16) {
-    const int grid_x = lay.n_tok / SKT + lay.n_req + 1;   // >= sum of per-request tile counts
-    scores_bf16<<<dim3(grid_x, hkv), 256, 0, stream>>>(
+    const int parts = score_parts(dims, lay.n_tok, lay.n_req);
+    scores_bf16<<<dim3(score_tiles(lay.n_tok, lay.n_req), parts), 256, 0, stream>>>(
         (const uint16_t*)q, q_index, sq_rows, sq_start, lse, lse_index, lay, kv.n_pages,
-        (const uint16_t*)kv.k, hq, hkv, partial, kLog2e / sqrtf((float)d));
+        (const uint16_t*)kv.k, hq, hkv, partial, kLog2e / sqrtf((float)d), hq / parts);
   } else {
     dim3 grid((lay.n_tok + 255) / 256, hkv);
     const float scale = 1.f / sqrtf((float)d);

@@ -58,7 +58,12 @@ size_t decode_ws_bytes(const sx_dims& d, int n_tok, int n_req);
 sx_status launch_decode(const sx_dims& dims, const sx_layout& lay, const void* q, const sx_pages& kv,
                         void* o, float* lse, void* ws, hipStream_t stream);
 
-// Per-(kv head, token) partial attention-mass scores of the Sparse-Q rows.
+// Partial score rows the score pass writes ([parts][n_tok]): one per kv head,
+// or per query head for bf16 prompts too short to fill the chip with kv-head
+// workgroups; the top-k adds them in row order.
+int score_parts(const sx_dims& d, int n_tok, int n_req);
+
+// Partial attention-mass scores of the Sparse-Q rows, per score_parts row.
 sx_status launch_scores(const sx_dims& dims, const sx_layout& lay, const void* q,
                         const int32_t* q_index, const int32_t* sq_rows, const int32_t* sq_start,
                         int n_sq, const float* lse, const int32_t* lse_index,
