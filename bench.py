@@ -155,10 +155,12 @@ def mfma_peak_measure(shapes=((2048, 400), (4096, 200), (8192, 100)), reps: int 
 
 def cpu_baseline(dims, plan, n_sparse: int, T: int, reused: int, seed: int = 4242):
     """The float64 oracle on a bounded sample of one sparse layer of the same
-    workload, scaled to tokens/s per layer.  Sample: realign of one
-    1920-token passage, projection of 16 active rows, attention of 8 active
-    rows, and 4 Sparse-Q rows of the selection probe (amortised over the
-    sparse layers); each part is scaled by its share of the layer's work."""
+    workload, scaled to tokens/s per layer.  Sample (10-30 s of CPU work):
+    realign of 16 of the 1920-token passages, projection of 1024 active rows,
+    attention of 2048 active rows, and 128 Sparse-Q rows of the selection
+    probe (amortised over the sparse layers); each part is scaled by its
+    share of the layer's work."""
+    n_pass, n_rec, n_att, n_probe = 16, 1024, 2048, 128
     import oracle
     from segment_level_kv_amd import synth
     try:
@@ -178,35 +180,43 @@ def cpu_baseline(dims, plan, n_sparse: int, T: int, reused: int, seed: int = 424
     K = synth.to_storage(rng.standard_normal((T, hkv, d)), "bf16")
     V = synth.to_storage(rng.standard_normal((T, hkv, d)), "bf16")
     t = {}
-    # realign: one passage
+    # realign: n_pass passages, each moved by its own offset
     t0 = time.perf_counter()
-    oracle.realign_segment(K[:1920], V[:1920], 512, 2048, dims.theta, "bf16")
-    t["realign"] = (time.perf_counter() - t0) * (R / 1920)
-    # recompute: 16 rows
-    x = synth.to_storage(synth._rmsnormed_gaussian(rng, 16, dims.hidden, dims.eps), "bf16")
+    for i in range(n_pass):
+        a = 512 + 1920 * i
+        oracle.realign_segment(K[a:a + 1920], V[a:a + 1920], a, 2048 + 1920 * i, dims.theta, "bf16")
+    t["realign"] = (time.perf_counter() - t0) * (R / (1920 * n_pass))
+    # recompute: n_rec rows
+    x = synth.to_storage(synth._rmsnormed_gaussian(rng, n_rec, dims.hidden, dims.eps), "bf16")
     wq, wk, wv = synth._weights(rng, dims)
     t0 = time.perf_counter()
-    oracle.project_rows(x, wq, wk, wv, S[:16], dims.theta, hq, hkv, d, "bf16")
-    t["recompute"] = (time.perf_counter() - t0) * (len(A) / 16)
-    # attention: 8 active rows, scaled by key count
-    rows = np.sort(rng.choice(A, size=8, replace=False))
-    q = synth.to_storage(rng.standard_normal((8, hq, d)), "bf16")
+    oracle.project_rows(x, wq, wk, wv, S[:n_rec], dims.theta, hq, hkv, d, "bf16")
+    t["recompute"] = (time.perf_counter() - t0) * (len(A) / n_rec)
+    # attention: n_att active rows, scaled by key count
+    rows = np.sort(rng.choice(A, size=n_att, replace=False))
+    q = synth.to_storage(rng.standard_normal((n_att, hq, d)), "bf16")
     t0 = time.perf_counter()
     oracle.causal_attention(q, rows, K, V)
     t["attn"] = (time.perf_counter() - t0) * (np.sum(A + 1) / np.sum(rows + 1))
-    # selection probe: 4 Sparse-Q rows (LSE + scores), amortised
-    qs = synth.to_storage(rng.standard_normal((4, hq, d)), "bf16")
+    # selection probe: n_probe Sparse-Q rows (LSE + scores), amortised
+    qs = synth.to_storage(rng.standard_normal((n_probe, hq, d)), "bf16")
     t0 = time.perf_counter()
-    _, lse = oracle.causal_attention(qs, sq[:4], K, V)
-    oracle.attention_mass_scores(qs, sq[:4], K, lse)
-    t["select"] = (time.perf_counter() - t0) * (len(sq) / 4) / n_sparse
+    _, lse = oracle.causal_attention(qs, sq[:n_probe], K, V)
+    oracle.attention_mass_scores(qs, sq[:n_probe], K, lse)
+    t["select"] = (time.perf_counter() - t0) * (len(sq) / n_probe) / n_sparse
+    sample_s = sum(t_ * f for t_, f in zip(
+        (t["realign"], t["recompute"], t["attn"], t["select"]),
+        (1920 * n_pass / R, n_rec / len(A), np.sum(rows + 1) / np.sum(A + 1),
+         n_probe * n_sparse / len(sq))))
     layer_s = sum(t.values())
     return {"value": T / layer_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": ("float64 NumPy oracle, one sparse layer of the same workload: realign of one "
-                       "1920-token passage (x R/1920), projection of 16 active rows (x |A|/16), "
-                       "attention of 8 active rows (x key-count share), 4 Sparse-Q probe rows "
-                       "(x 256/4, amortised over the sparse layers)"),
-            "seconds_per_layer": layer_s, "parts_s": {k_: round(v, 4) for k_, v in t.items()}}
+            "sample": (f"float64 NumPy oracle, one sparse layer of the same workload: realign of "
+                       f"{n_pass} 1920-token passages (x R/{1920 * n_pass}), projection of {n_rec} "
+                       f"active rows (x |A|/{n_rec}), attention of {n_att} active rows (x key-count "
+                       f"share), {n_probe} Sparse-Q probe rows (x {len(sq)}/{n_probe}, amortised "
+                       f"over the sparse layers)"),
+            "sample_cpu_seconds": round(float(sample_s), 2),
+            "seconds_per_layer": layer_s, "parts_s": {k_: round(float(v), 4) for k_, v in t.items()}}
 
 
 def sweep(args):
