@@ -5,9 +5,9 @@
 //   [q | k | v] = x[rows] . W_qkv^T ;  q, k rotated by R_pos ;
 //   k, v scattered into the request's pages, q written densely.
 //
-// bf16 path: MFMA GEMM (v_mfma_f32_32x32x16_bf16), 256x128 output tiles
-// (one tile column = one head of 128, so both halves of every rotate-half
-// pair are in the tile).  Tiles are assigned XCD-contiguously (workgroup b
+// bf16 path: MFMA GEMM (v_mfma_f32_32x32x16_bf16), 256x128 or 256x256
+// output tiles (one or two whole heads of 128, so both halves of every
+// rotate-half pair are in the tile).  Tiles are assigned XCD-contiguously (workgroup b
 // runs on XCD b % 8) and grouped 4 row-tiles at a time so that concurrently
 // running workgroups share W and X slices in their XCD's L2.  The epilogue
 // stages the fp32 tile in LDS, applies RoPE with the fp64-built table,
@@ -31,21 +31,33 @@ constexpr int GROUP_M = 4;
 // MFMA tiles of 32 x 32 (one wave's barrier and LDS waits overlap the other's
 // MFMAs; four waves of 128 x 64 were 7% slower); the operands of k-slice ks+1
 // are read from LDS while the MFMAs of slice ks run.
-constexpr int BM2 = 256, NST2 = 3;
+constexpr int BM2 = 256;
 constexpr int GW = 8;                  // waves per workgroup: two per SIMD
 constexpr int GT = 64 * GW;            // threads per workgroup
-constexpr int WROWS = BM2 / (GW / 2);  // output rows per wave (waves are (GW/2) x 2)
-constexpr int MI = WROWS / 32;         // 32 x 32 MFMA tiles per wave along M
 constexpr int NCA = BM2 * BK * 2 / 1024 / GW;   // 1 KB stage copies per wave: A
-constexpr int NCB = BN * BK * 2 / 1024 / GW;    //                              B
+// HPT heads (128 columns each) per tile.  HPT = 1: a ring of 3 stages, waves
+// 4 x 2 of 64 x 64.  HPT = 2 (256 x 256 tiles, 1.5x the flops per staged
+// byte): stages of 64 KB, so a ring of 2, waves 2 x 4 of 128 x 64.
+template <int HPT>
+struct GemmCfg {
+  static constexpr int BNT = BN * HPT;              // output columns per tile
+  static constexpr int NST = HPT == 1 ? 3 : 2;      // ring stages
+  static constexpr int WGN = 2 * HPT;               // waves along N (64 columns each)
+  static constexpr int WGM = GW / WGN;              // waves along M
+  static constexpr int WROWS = BM2 / WGM;           // output rows per wave
+  static constexpr int MI = WROWS / 32;             // 32 x 32 MFMA tiles per wave along M
+  static constexpr int NCB = BNT * BK * 2 / 1024 / GW;   // 1 KB stage copies per wave: B
+};
+template <int HPT>
 struct Gemm2Stage {
   uint16_t a[BM2][BK];
-  uint16_t b[BN][BK];
+  uint16_t b[BN * HPT][BK];
 };
+template <int HPT>
 struct Gemm2Smem {
   union {
-    Gemm2Stage st[NST2];
-    float c[BM2][LDC];
+    Gemm2Stage<HPT> st[GemmCfg<HPT>::NST];
+    float c[BM2][LDC];                 // one head of the output tile at a time
   };
   // per output row, resolved once per tile: page of the token (-1 if the row
   // or its page is invalid; for Q heads only row_ok matters), its slot and
@@ -56,15 +68,18 @@ struct Gemm2Smem {
   int32_t row_ok[BM2];
 };
 
+template <int HPT>
 __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
     const uint16_t* __restrict__ x, int hidden, const int32_t* __restrict__ rows, int n_rows,
     const uint16_t* __restrict__ w, int head0, int n_tiles_m, int n_tiles_n, sx_layout lay,
     int n_pages, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
     uint16_t* __restrict__ q_out, int hq, int hkv) {
+  using Cfg = GemmCfg<HPT>;
+  constexpr int NST2 = Cfg::NST, WROWS = Cfg::WROWS, MI = Cfg::MI, NCB = Cfg::NCB;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  Gemm2Smem& sm = *reinterpret_cast<Gemm2Smem*>(smem_raw);
+  Gemm2Smem<HPT>& sm = *reinterpret_cast<Gemm2Smem<HPT>*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 
   // ---- tile assignment: XCD-contiguous ranges, grouped along M ----------
   const int total = n_tiles_m * n_tiles_n;
@@ -78,8 +93,8 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
   const int mt = first_m + within % gsz;
   const int nt = within / gsz;
   const int m0 = mt * BM2;
-  const int head = head0 + nt;                 // 0..hq-1: Q, then K heads, then V heads
-  const uint16_t* wt = w + (size_t)head * 128 * hidden;
+  const int head1 = head0 + HPT * nt;         // first head: 0..hq-1 Q, then K heads, then V heads
+  const uint16_t* wt = w + (size_t)head1 * 128 * hidden;
 
   if (tid < BM2) {
     int r = -1, idx = 0;
@@ -144,15 +159,15 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   const int lr = lane & 31, lh = lane >> 5;
-  issue(0, 0);
-  issue(1, 1);
+#pragma unroll
+  for (int s = 0; s < NST2 - 1; ++s) issue(s, s);
   for (int kt = 0; kt < n_k; ++kt) {
     const int slot = kt % NST2;
-    // stage kt resident in every wave (stage kt+1's copies may be in
-    // flight); the slot of stage kt-1 is free for stage kt+2
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NCA + NCB) : "memory");
-    issue(kt + 2, (kt + 2) % NST2);
-    const Gemm2Stage& S = sm.st[slot];
+    // stage kt resident in every wave (the NST2 - 2 stages after it may be
+    // in flight); the slot of stage kt-1 is free for stage kt+NST2-1
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NST2 - 2) * (NCA + NCB)) : "memory");
+    issue(kt + NST2 - 1, (kt + NST2 - 1) % NST2);
+    const Gemm2Stage<HPT>& S = sm.st[slot];
     // Operands of k-slice ks+1 are read while the MFMAs of slice ks run.
     bf16x8 af[2][MI], bfr[2][2];
     auto load = [&](int ks, int buf) __attribute__((always_inline)) {
@@ -183,18 +198,23 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
   // all copies landed and every wave done with the ring before it becomes C
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // ---- epilogue: fp32 tile -> LDS ------------------------------------------
+  // ---- epilogue, one head at a time: its fp32 columns -> LDS -------------
+  for (int h = 0; h < HPT; ++h) {
+  if (h > 0) __syncthreads();                  // every thread done with the previous head
+  if (wn / 2 == h) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * WROWS + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int c = wn * 64 + j * 32 + (lane & 31);
-        sm.c[r][c] = acc[i][j][v];
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * WROWS + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int c = (wn & 1) * 64 + j * 32 + (lane & 31);
+          sm.c[r][c] = acc[i][j][v];
+        }
+  }
   __syncthreads();
+  const int head = head1 + h;
 
   if (head < hq + hkv) {
     // Q or K head: rotate-half pairs (e, e+64), 8 pairs per unit; a thread
@@ -257,6 +277,7 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
         for (int i = 0; i < 4; ++i) base[(e + i) * kPage] = f2bf(c4[i]);
       }
     }
+  }
   }
 }
 
@@ -429,6 +450,21 @@ __global__ __launch_bounds__(128) void qkv_rows_f32(
   }
 }
 
+// Two heads per tile or one: one workgroup fills a compute unit (256 of
+// them), so the launch takes about ceil(tiles / 256) rounds, and a two-head
+// tile takes about 1.8x a one-head tile (measured: 1.45 against 1.61 ms for
+// 31,488 rows, i.e. 2 x 0.90).  Two heads when that round count is lower,
+// e.g. for a full layer's QKV; one for a few thousand rows, where two-head
+// tiles would leave the last round mostly idle (3,379 rows: 0.251 against
+// 0.216 ms).
+constexpr int kGemmCUs = 256;
+bool gemm_two_heads(int mt, int n_heads) {
+  if (n_heads % 2 != 0) return false;
+  const long long t1 = (long long)mt * n_heads, t2 = t1 / 2;
+  const long long r1 = (t1 + kGemmCUs - 1) / kGemmCUs, r2 = (t2 + kGemmCUs - 1) / kGemmCUs;
+  return 9 * r2 < 5 * r1;
+}
+
 }  // namespace
 
 sx_status launch_recompute(const sx_dims& dims, const sx_layout& lay, const void* x,
@@ -451,14 +487,20 @@ sx_status launch_recompute(const sx_dims& dims, const sx_layout& lay, const void
     else go(qkv_skinny_bf16<4>);
   } else if (dims.dtype == SX_BF16) {
     const int mt = (n_rows + BM2 - 1) / BM2;
-    const int total = mt * n_heads;
-    const int grid = ((total + 7) / 8) * 8;
-    const size_t smem = sizeof(Gemm2Smem);
-    const sx_status st = allow_lds((const void*)qkv_gemm256_bf16, smem, "sx_recompute_kv");
+    auto go = [&](auto kernel, int hpt, size_t smem) -> sx_status {
+      const int nt = n_heads / hpt;
+      const int grid = ((mt * nt + 7) / 8) * 8;
+      const sx_status st = allow_lds((const void*)kernel, smem, "sx_recompute_kv");
+      if (st != SX_OK) return st;
+      kernel<<<grid, GT, smem, stream>>>(
+          (const uint16_t*)x, dims.hidden, rows, n_rows, (const uint16_t*)w_qkv, head0, mt, nt,
+          lay, kv.n_pages, (uint16_t*)kv.k, (uint16_t*)kv.v, (uint16_t*)q_out, hq, hkv);
+      return SX_OK;
+    };
+    const sx_status st = gemm_two_heads(mt, n_heads)
+                             ? go(qkv_gemm256_bf16<2>, 2, sizeof(Gemm2Smem<2>))
+                             : go(qkv_gemm256_bf16<1>, 1, sizeof(Gemm2Smem<1>));
     if (st != SX_OK) return st;
-    qkv_gemm256_bf16<<<grid, GT, smem, stream>>>(
-        (const uint16_t*)x, dims.hidden, rows, n_rows, (const uint16_t*)w_qkv, head0, mt, n_heads,
-        lay, kv.n_pages, (uint16_t*)kv.k, (uint16_t*)kv.v, (uint16_t*)q_out, hq, hkv);
   } else {
     dim3 grid(n_rows, n_heads);
     const size_t smem = (size_t)dims.hidden * sizeof(float);

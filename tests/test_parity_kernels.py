@@ -182,6 +182,66 @@ def test_recompute_parity_and_scatter(shape, n_rows):
                 assert np.array_equal(after_v[p, :, :, sl], before_v[p, :, :, sl])
 
 
+def test_recompute_two_heads_per_tile_sampled():
+    """Row counts whose launch takes 256 x 256 tiles (two heads per tile):
+    5,200 of 6,000 tokens in Llama shapes, once with Q (48 heads) and once
+    K/V only (16 heads).  The oracle projects 320 sampled rows, spread over
+    every row tile and including the last, partial one; both heads of every
+    tile are compared, and exactly the listed rows' slots are written."""
+    dims = SHAPES["llama"]
+    n_rows = 5200
+    say(f"[recompute] two heads per tile: rows={n_rows}")
+    rng = np.random.default_rng(23)
+    seq = np.array([0, 4000, 6000], np.int32)
+    n_tok = int(seq[-1])
+    x = _store(synth._rmsnormed_gaussian(rng, n_tok, dims.hidden, dims.eps), dims)
+    case_w = synth._weights(rng, dims)
+    w = np.concatenate(case_w, axis=0)
+    rows = np.sort(rng.choice(n_tok, size=n_rows, replace=False)).astype(np.int32)
+    rng.shuffle(rows)
+    n_pages = 2 * 250 + 8
+    perm = rng.permutation(n_pages).astype(np.int32)
+    bt = perm[:2 * 250].reshape(2, 250)
+    rope = LY.rope_table(dims.theta, dims.head_dim, 6200, DEV)
+    pos_off = np.array([0, 131], np.int32)
+    lay = LY.DeviceLayout(seq, bt, rope, DEV, pos_offset=pos_off)
+    dt = LY.storage_dtype(dims.dtype)
+    xt = torch.from_numpy(x).to(dt).to(DEV)
+    wt = torch.from_numpy(w).to(dt).to(DEV)
+    rt = torch.from_numpy(rows).to(DEV)
+    req = (rows >= 4000).astype(int)
+    idx = rows - seq[req]
+    sample = np.unique(np.concatenate([np.arange(0, n_rows, 17), np.arange(n_rows - 64, n_rows)]))
+    sample = sample[np.linspace(0, len(sample) - 1, 320).astype(int)]
+    sample = np.union1d(sample, np.arange(n_rows - 16, n_rows))
+    s_rows = rows[sample]
+    qr, kr, vr = oracle.project_rows(x[s_rows], case_w[0], case_w[1], case_w[2],
+                                     idx[sample] + pos_off[req[sample]], dims.theta,
+                                     dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.dtype)
+    for with_q in (True, False):
+        pool = LY.PagePool.alloc(n_pages, dims, DEV)
+        q = torch.full((n_rows, dims.n_q_heads, dims.head_dim), 7.0, dtype=dt, device=DEV) if with_q else None
+        before_k, before_v = _bits(pool.k), _bits(pool.v)
+        L.sx_recompute_kv(LY.make_dims(dims), lay.struct, xt, rt, n_rows, wt, pool.struct(), q)
+        torch.cuda.synchronize()
+        ak, av = _pool_host(pool)
+        kg = np.stack([ak[bt[r, i // 16], :, i % 16, :] for r, i in zip(req[sample], idx[sample])])
+        vg = np.stack([av[bt[r, i // 16], :, :, i % 16] for r, i in zip(req[sample], idx[sample])])
+        pairs = [(kg, kr, "K"), (vg, vr, "V")]
+        if with_q:
+            pairs.append((q.float().cpu().double().numpy()[sample], qr, "Q"))
+        for g_, r_, nm in pairs:
+            big = np.abs(r_) >= 1e-2
+            assert bf16_ulps(g_[big], r_[big]).max() <= 1, nm
+            assert_close_bf16(g_, r_, rel=BF16_STEP_REL, what=f"{nm} (with_q={with_q})")
+        after_k, after_v = _bits(pool.k), _bits(pool.v)
+        hit = np.zeros((n_pages, 16), dtype=bool)
+        hit[bt[req, idx // 16], idx % 16] = True
+        changed_k = np.any(after_k != before_k, axis=(1, 3))          # [page, slot]
+        changed_v = np.any(after_v != before_v, axis=(1, 2))
+        assert not np.any(changed_k & ~hit) and not np.any(changed_v & ~hit)
+
+
 # ---------------------------------------------------------------- attention --
 
 def _attn_inputs(dims, lens, seed):
