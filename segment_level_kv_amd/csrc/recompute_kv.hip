@@ -23,21 +23,22 @@ constexpr int BN = 128, BK = 64;
 constexpr int LDC = BN + 4;          // padded fp32 row of the staged output tile
 constexpr int GROUP_M = 4;
 
-// bf16 GEMM, 256 x 128 output tiles (256 rows, one head).  K-steps of 64
-// go global -> LDS directly (global_load_lds_dwordx4) into a ring of three
-// stages; each 128-byte LDS row keeps its 16-byte chunk c at position
-// c ^ (row & 7), so the 32 rows an MFMA operand read touches spread over
-// all banks.  Eight waves, two per SIMD, each 64 rows x 64 columns = 2 x 2
-// MFMA tiles of 32 x 32 (one wave's barrier and LDS waits overlap the other's
-// MFMAs; four waves of 128 x 64 were 7% slower); the operands of k-slice ks+1
-// are read from LDS while the MFMAs of slice ks run.
+// bf16 GEMM, 256-row output tiles of one or two heads.  K-steps of 64 go
+// global -> LDS directly (global_load_lds_dwordx4) into a ring of stages;
+// each 128-byte LDS row keeps its 16-byte chunk c at position c ^ (row & 7),
+// so the rows an MFMA operand read touches spread over the banks.  Eight
+// waves, two per SIMD, each of 64 columns and 64 or 128 rows in 32 x 32
+// MFMA tiles (one wave's barrier and LDS waits overlap the other's MFMAs;
+// for one head, four waves of 128 x 64 were 7% slower than eight of
+// 64 x 64); the operands of k-slice ks+1 are read from LDS while the MFMAs
+// of slice ks run.
 constexpr int BM2 = 256;
 constexpr int GW = 8;                  // waves per workgroup: two per SIMD
 constexpr int GT = 64 * GW;            // threads per workgroup
 constexpr int NCA = BM2 * BK * 2 / 1024 / GW;   // 1 KB stage copies per wave: A
-// HPT heads (128 columns each) per tile.  HPT = 1: a ring of 3 stages, waves
-// 4 x 2 of 64 x 64.  HPT = 2 (256 x 256 tiles, 1.5x the flops per staged
-// byte): stages of 64 KB, so a ring of 2, waves 2 x 4 of 128 x 64.
+// HPT heads (128 columns each) per tile.  HPT = 1: 48 KB stages in a ring
+// of 3, waves 4 x 2 of 64 x 64.  HPT = 2 (256 x 256 tiles, 1.5x the flops
+// per staged byte): 64 KB stages in a ring of 2, waves 2 x 4 of 128 x 64.
 template <int HPT>
 struct GemmCfg {
   static constexpr int BNT = BN * HPT;              // output columns per tile
