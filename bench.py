@@ -231,7 +231,7 @@ def sweep(args):
     seg_lengths, layout, p_src = synth.chat_layout()
     seg_len = {i: n for i, n in enumerate(seg_lengths)}
     seg_p = {i: p for i, p in enumerate(p_src)}
-    n_layers = args.layers
+    n_layers = args.layers if args.layers is not None else 32
     T = sum(seg_len[v] if k == "reuse" else v for k, v in layout)
     n_cache = sum(seg_lengths)
     ratio = (10, 100)
