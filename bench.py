@@ -439,7 +439,7 @@ def main():
         },
         "attn_pct_mfma_bf16_peak": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
         "roofline": {
-            "kernel": ("sx_sparse_attn_run (attn_fwd<true,1>; attn_merge only when tiles are split), one "
+            "kernel": ("sx_sparse_attn_run (attn_fwd<true>; attn_merge only when tiles are split), one "
                        "launch per sparse layer over the work list sx_sparse_attn_plan builds once per pass"),
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -17,17 +17,17 @@
 // do not depend on scheduling.
 //
 // Per 32-key sub-block and wave (32 pairs):
-//   S^T[key][pair] = K . Q^T    8 x v_mfma_f32_32x32x16_bf16, Q in AGPRs
+//   S^T[key][pair] = K . Q^T    8 x v_mfma_f32_32x32x16_bf16 (one chain)
 //   online softmax over the key axis, which lies inside a lane (16 keys per
 //   lane and pair, the other 16 in the partner lane half)
 //   O^T[d][pair] += V^T . P^T   8 x v_mfma_f32_32x32x16_bf16
-// Keys are permuted inside each 32-key sub-block when K is read from LDS so
-// that the S^T accumulators are directly the B operand of the PV product.
-// A step issues QK^T of sub-block j+2, PV of j and the softmax of j+1, which
-// are independent; the two waves of a SIMD run the MFMA and softmax phases
-// in opposite orders.  The running maximum is raised only when a block's
-// maximum exceeds it by more than 2^8 (in the exp2 domain), so O is rarely
-// rescaled; exp2 arguments then stay below 8.
+// Q, O, S and P all live in VGPRs (no AGPR copies, no scratch).  Keys are
+// permuted inside each 32-key sub-block when K is read from LDS so that the
+// S^T accumulators are directly the B operand of the PV product.  A step
+// issues PV of sub-block j, QK^T of j+2 and the softmax of j+1, which are
+// independent, as one scheduling region.  The running maximum is raised
+// only when a block's maximum exceeds it by more than 2^8 (in the exp2
+// domain), so O is rarely rescaled; exp2 arguments then stay below 8.
 // K/V stream through a 4-stage LDS ring of 64-key stages (global -> LDS
 // directly, one barrier per stage); the page ids of a stage are
 // wave-uniform and come through the scalar cache.  Workgroup b takes kv head
@@ -43,11 +43,7 @@ namespace sx {
 namespace {
 
 constexpr int KB = 64;                 // keys per block
-constexpr int NSTAGE = 4;
-#ifndef SX_ATTN_HALVES
-#define SX_ATTN_HALVES 1
-#endif
-constexpr int kHalvesPerWave = SX_ATTN_HALVES;   // query halves of 32 pairs per wave (1 or 2)              // LDS ring depth (copies issued 2 stages ahead)
+constexpr int NSTAGE = 4;              // LDS ring depth (copies issued 3 stages ahead)
 constexpr int PAIRS = 256;             // (row, head) pairs per workgroup
 constexpr int kTargetItems = 256;      // work items aimed for (one per CU); tiles are split only below it
 constexpr int kMinChunk = 1024;        // shortest key chunk of a split tile
@@ -92,7 +88,7 @@ WsLayout ws_layout(int n_rows, int n_req, int G, int hkv, bool with_o) {
   w.tiles = off;    off += align256((size_t)w.max_tiles * sizeof(TileInfo));
   w.items = off;    off += align256((size_t)w.max_items * sizeof(AttnItem));
   w.merges = off;   off += align256((size_t)w.max_tiles * sizeof(MergeTile));
-  w.part_ml = off;  off += align256((size_t)w.max_items * hkv * PAIRS * 2 * sizeof(float));
+  w.part_ml = off;  off += align256((size_t)w.max_items * hkv * PAIRS * 4 * sizeof(float));
   w.part_o = off;
   if (with_o) off += align256((size_t)w.max_items * hkv * PAIRS * 128 * sizeof(uint16_t));
   w.total = off;
@@ -320,11 +316,11 @@ __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
-// NB query halves (32 pairs each) per wave; 8 / NB waves share a tile of
-// 256 pairs.  NB = 1 puts two waves on each SIMD, so one wave's softmax and
-// LDS latency overlap the other's MFMAs.
-template <bool WITH_O, int NB>
-__global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
+// One workgroup: 8 waves of 32 (row, head) pairs each, two waves per SIMD.
+// Per 32-key sub-block and wave: 8 MFMAs of Q K^T, 8 of P V, 17
+// exponentials and about 65 other VALU operations.
+template <bool WITH_O>
+__global__ __launch_bounds__(512, 1) void attn_fwd(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_index,
     const int32_t* __restrict__ rows, sx_layout lay, int n_pages,
     const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool, int hkv, int G,
@@ -336,7 +332,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
 
   const int g = blockIdx.x % hkv;
   const int ii = blockIdx.x / hkv;
-  if (ii >= counters[0] || n_pages <= 0) return;
+  if (ii >= counters[0] || n_pages <= 0 || lay.max_pages <= 0) return;
   const AttnItem it = items[ii];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hl = lane >> 5;
   const int hq = G * hkv;
@@ -347,37 +343,33 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
   const int k1 = min(it.k1, seq_len);
   if (k1 <= k0) return;
 
-  // ---- this lane's NB pairs: query operand and positions --------------------
-  constexpr int NW = 8 / NB;               // waves per workgroup
-  constexpr int NT = 64 * NW;              // threads per workgroup
+  // ---- this lane's (row, head) pair: query operand and position -------------
+  constexpr int NT = 512;                  // threads per workgroup
   const int npairs = it.nrows * G;
-  int pos_q[NB];
-  bf16x8 qf[NB][8];
-  const uint16_t* qptr[NB];
-  int wave_pmin = 0x7fffffff;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int p = 32 * NB * w + 32 * nb + (lane & 31);
-    const bool valid = p < npairs;
-    const int r = p / G, hh = p - r * G;
+  const int pair = 32 * w + (lane & 31);
+  int pos_q;
+  const uint16_t* qptr;
+  {
+    const bool valid = pair < npairs;
+    const int r = pair / G, hh = pair - r * G;
     const int m = it.row0 + (valid ? r : 0);
     const int row_tok = rows ? rows[m] : m;
     // Causal limit, clamped to the item's last key: the sub-blocks the
     // pipeline runs past the item's end are then masked for every pair.
-    pos_q[nb] = valid ? min(row_tok - seq0, k1 - 1) : k1 - 1;
-    wave_pmin = min(wave_pmin, pos_q[nb]);
+    pos_q = valid ? min(row_tok - seq0, k1 - 1) : k1 - 1;
     // (A pair past the tile reads a valid row's Q; its results are never
     // stored.)
-    qptr[nb] = q + ((size_t)(q_index ? q_index[m] : m) * hq + g * G + hh) * 128 + hl * 8;
+    qptr = q + ((size_t)(q_index ? q_index[m] : m) * hq + g * G + hh) * 128 + hl * 8;
   }
+  int wave_pmin = pos_q;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wave_pmin = min(wave_pmin, __shfl_xor(wave_pmin, off));
 
   // ---- K/V stages: global -> LDS directly (global_load_lds_dwordx4) ---------
   // A wave instruction writes 64 x 16 B = 1 KB of LDS, lane L at byte 16 L.
-  // Each wave copies NB/2 of a page of each 64-key block (K rows 8*NB*w ..,
-  // and the matching head dimensions of its V page-head), 2*NB KB of K and
-  // of V, so page ids are wave-uniform and per-lane offsets are constants.
+  // Each wave copies half a page of each 64-key block (K rows 8w .. 8w+7,
+  // and the matching 64 head dimensions of its V page-head), 2 KB of K and
+  // 2 KB of V, so page ids are wave-uniform and per-lane offsets constants.
   // K stage: 64 key rows x 256 B; row R keeps 16-byte chunk c at slot
   //   c ^ (R & 15) (16 rows read together hit 16 distinct bank groups).
   // V stage: the page layout itself, [4 pages][128 d][16 keys]; row d keeps
@@ -386,11 +378,11 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
   // data, masked or zeroed); an invalid page id reads page 0.
   const int32_t* bt = lay.block_table + (size_t)req * lay.max_pages;
   const int kmax = k1 - 1;                 // last key of this item
-  const int last_pi = min(kmax / kPage, lay.max_pages - 1);
+  const int last_pi = max(min(kmax / kPage, lay.max_pages - 1), 0);
   typedef __attribute__((address_space(1))) const void* gptr_t;
   typedef __attribute__((address_space(3))) void* lptr_t;
-  constexpr int NCP = 2 * NB;              // copies of 1 KB per wave for K (and for V)
-  const int wpart = NB == 2 ? 0 : (w & 1);  // which half of its page a wave copies
+  constexpr int NCP = 2;                   // copies of 1 KB per wave for K (and for V)
+  const int wpart = w & 1;                 // which half of its page a wave copies
   uint32_t koff[NCP], voff[NCP];           // byte offsets inside a page-head
 #pragma unroll
   for (int i = 0; i < NCP; ++i) {
@@ -410,7 +402,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
   const int wu = __builtin_amdgcn_readfirstlane(w);
   typedef __attribute__((address_space(4))) const int32_t* cptr_t;
   const cptr_t btc = (cptr_t)bt;
-  const int wpage = wu / (2 / NB);          // this wave's page of a block
+  const int wpage = wu >> 1;                // this wave's page of a block
   auto page_of_block = [&](int kb) __attribute__((always_inline)) {
     const int pi = min(kb / kPage + wpage, last_pi);
     const int pg = btc[pi];
@@ -421,7 +413,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
   auto issue_k = [&](int pg, int s) __attribute__((always_inline)) {
     const size_t base = ((size_t)pg * hkv + g) * head_bytes;
     const unsigned char* kp = reinterpret_cast<const unsigned char*>(kpool) + base;
-    unsigned char* kst = reinterpret_cast<unsigned char*>(&st[s].k[8 * NB * wu][0]);
+    unsigned char* kst = reinterpret_cast<unsigned char*>(&st[s].k[8 * wu][0]);
 #pragma unroll
     for (int i = 0; i < NCP; ++i)
       __builtin_amdgcn_global_load_lds((gptr_t)(kp + koff[i]), (lptr_t)(kst + i * 1024), 16, 0, 0);
@@ -430,8 +422,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
     if (!WITH_O) return;
     const size_t base = ((size_t)pg * hkv + g) * head_bytes;
     const unsigned char* vp = reinterpret_cast<const unsigned char*>(vpool) + base;
-    unsigned char* vst =
-        reinterpret_cast<unsigned char*>(&st[s].v[wpage][NB == 2 ? 0 : 64 * (wu & 1)][0]);
+    unsigned char* vst = reinterpret_cast<unsigned char*>(&st[s].v[wpage][64 * (wu & 1)][0]);
 #pragma unroll
     for (int i = 0; i < NCP; ++i)
       __builtin_amdgcn_global_load_lds((gptr_t)(vp + voff[i]), (lptr_t)(vst + i * 1024), 16, 0, 0);
@@ -454,6 +445,20 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
       vs[(j * 128 + d) * kPage + half * 8 + (kk & 7)] = 0;
     }
   };
+  // The barrier asm above waits for every LDS and scalar load (lgkmcnt(0)),
+  // but the compiler does not read asm: this real s_waitcnt lgkmcnt(0) (no
+  // cost right after it) tells its wait insertion that the scalar page-id
+  // loads are done.  With a scalar load pending, scalar results may return
+  // out of order with LDS reads, so every wait for an LDS read would have to
+  // be lgkmcnt(0) and drain all of the step's LDS reads in flight.
+  auto lgkm_settled = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63, expcnt 7, lgkmcnt 0 (gfx9 encoding)
+  };
+  // Workgroup barrier after this wave's LDS writes, leaving the stage copies
+  // in flight.
+  auto lds_barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
 
   // K row read by this lane for the S^T A operand: inside a 32-key sub-block
   // the MFMA row mrow holds key kperm(mrow), so that accumulator register v
@@ -471,30 +476,7 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
       kf[kk] = *reinterpret_cast<const bf16x8*>(kr + slot * 8);
     }
   };
-  // S^T of one query half nb (32 pairs) for a sub-block: 8 MFMAs.
-  auto qk_half = [&](const bf16x8 (&kf)[8], int nb, f32x16& S) __attribute__((always_inline)) {
-    S = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[nb][kk], S, 0, 0, 0);
-  };
-
-  f32x16 oacc[4][NB];
-#pragma unroll
-  for (int md = 0; md < 4; ++md)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) oacc[md][nb] = f32x16{};
-  float m_run[NB], alpha[NB];                // running max (raw logit units), O scale
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) { m_run[nb] = -INFINITY; alpha[nb] = 1.f; }
-  // Running row sums as four partial sums per half (short add chains); the
-  // first add of each chain is an fma with alpha, which rescales them.
-  float lp[NB][4];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) lp[nb][0] = lp[nb][1] = lp[nb][2] = lp[nb][3] = 0.f;
-  const float c = scale_log2;
-
-  // V^T operand of sub-block h of stage s: 8 x 16 B (all loaded before the
-  // MFMAs that use them, so LDS latency is not paid per MFMA pair).
+  // V^T operand of sub-block h of stage s: 8 x 16 B.
   auto load_v = [&](int s, int h, bf16x8 (&vf)[8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -505,36 +487,45 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
         vf[ks * 4 + md] = *reinterpret_cast<const bf16x8*>(&st[s].v[2 * h + ks][d][half * 8]);
       }
   };
-  // O^T += V^T . P^T for one sub-block: 16 MFMAs.  Written as asm so that
-  // they accumulate in AGPRs while the QK^T MFMAs (compiler-selected, VGPR
-  // form) leave S in VGPRs for the softmax.  The compiler does not see these
-  // as MFMAs, so the code around them keeps the hazard distances itself:
-  // P is last written >= 4 wait states before (s_nop in the P pin), O is
-  // read only after >= 18 wait states (rescale and epilogue padding).
+
+  bf16x8 qf[8];                            // Q^T operand, 32 pairs x 128 d
+  f32x16 oacc[4];                          // O^T, 128 d x 32 pairs
 #pragma unroll
-  for (int md = 0; md < 4; ++md)
+  for (int md = 0; md < 4; ++md) oacc[md] = f32x16{};
+  bf16x8 vf[8];                            // V^T operand of the next P V
+  float m_run = -INFINITY, alpha = 1.f;    // running max (raw logit units), O scale
+  // Running row sums as four partial sums (short add chains); the first add
+  // of each chain is an fma with alpha, which rescales them.
+  float lp[4] = {0.f, 0.f, 0.f, 0.f};
+  const float c = scale_log2;
+
+  // S^T of a sub-block: 8 MFMAs, one dependent chain (gfx950 runs a chain
+  // on one accumulator faster than MFMAs alternating between accumulators).
+  auto qk = [&](const bf16x8 (&kf)[8], f32x16& S) __attribute__((always_inline)) {
+    S = f32x16{};
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(oacc[md][nb]));
-  auto pv_mfma = [&](const bf16x8 (&vf)[8], const bf16x8 (&P)[NB][2]) __attribute__((always_inline)) {
+    for (int kk = 0; kk < 8; ++kk) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], S, 0, 0, 0);
+  };
+  // O^T += V^T . P^T for one sub-block: 8 MFMAs, two in a row on each
+  // accumulator.
+  auto pv = [&](const bf16x8 (&P)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int md = 0; md < 4; ++md)
 #pragma unroll
-      for (int md = 0; md < 4; ++md)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(oacc[md][nb]) : "v"(vf[ks * 4 + md]), "v"(P[nb][ks]));
+      for (int ks = 0; ks < 2; ++ks)
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks * 4 + md], P[ks], oacc[md], 0, 0, 0);
   };
 
-  // Softmax of one query half of a sub-block (keys kb .. kb+31): S -> P (bf16,
-  // B operand of PV).  The running max of the half is raised only when the
-  // sub-block exceeds it by more than 2^8 in the exp2 domain (alpha[nb] is
-  // then the O scale factor).  Returns true if O's half must be rescaled.
-  auto softmax_half = [&](f32x16& S, bool mask, int kb, int nb, bf16x8 (&P)[2]) __attribute__((always_inline)) {
+  // Softmax of a sub-block (keys kb .. kb+31): S -> P (bf16, B operand of
+  // PV).  The running max is raised only when the sub-block exceeds it by
+  // more than 2^8 in the exp2 domain (alpha is then the O scale factor).
+  // Returns true if O must be rescaled.
+  auto softmax = [&](f32x16& S, bool mask, int kb, bf16x8 (&P)[2]) __attribute__((always_inline)) {
     if (mask) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = kb + 16 * (v >> 3) + 8 * hl + (v & 7);
-        S[v] = key > pos_q[nb] ? -INFINITY : S[v];
+        S[v] = key > pos_q ? -INFINITY : S[v];
       }
     }
     // tree of 3-input maxima (8 v_max3, depth 3)
@@ -544,93 +535,64 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
     const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]);
     const float u1 = fmaxf(fmaxf(t[3], t[4]), S[15]);
     const float mx = half_max(fmaxf(u0, u1));
-    const bool any = __ballot((mx - m_run[nb]) * c > 8.f) != 0ull;
-    const float m_new = any ? fmaxf(m_run[nb], mx) : m_run[nb];
+    const bool any = __ballot((mx - m_run) * c > 8.f) != 0ull;
+    const float m_new = any ? fmaxf(m_run, mx) : m_run;
     // A key chunk of a split tile can lie wholly past a row's position: the
     // row then has no key yet, m stays -inf, and the exponent reference is 0
     // (p = 0, alpha = 0) instead of -inf - -inf.  Only masked steps can see
     // such a row.
     const float m_ref = (mask && m_new == -INFINITY) ? 0.f : m_new;
-    alpha[nb] = __builtin_amdgcn_exp2f((m_run[nb] - m_ref) * c);
-    m_run[nb] = m_new;
+    alpha = __builtin_amdgcn_exp2f((m_run - m_ref) * c);
+    m_run = m_new;
     const float mc = m_ref * c;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      float p[8];
+      float pv_[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(fmaf(S[ks * 8 + i], c, -mc));
-        lp[nb][i & 3] = (ks == 0 && i < 4) ? fmaf(lp[nb][i & 3], alpha[nb], p[i]) : lp[nb][i & 3] + p[i];
+        pv_[i] = __builtin_amdgcn_exp2f(fmaf(S[ks * 8 + i], c, -mc));
+        lp[i & 3] = (ks == 0 && i < 4) ? fmaf(lp[i & 3], alpha, pv_[i]) : lp[i & 3] + pv_[i];
       }
       u32x4 pk;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = pack_bf2(p[2 * i], p[2 * i + 1]);
+      for (int i = 0; i < 4; ++i) pk[i] = pack_bf2(pv_[2 * i], pv_[2 * i + 1]);
       P[ks] = __builtin_bit_cast(bf16x8, pk);
     }
     return any;
   };
-  // O[:, nb] *= alpha[nb].  The empty volatile asm keeps this a real (rarely
-  // taken) branch: the compiler would otherwise speculate the 64 multiplies,
-  // which on AGPR accumulators cost 3 instructions each, into every step.
-  // The accumulators stay in AGPRs: the MFMAs read and write them there.
-  auto rescale_half = [&](int nb) __attribute__((always_inline)) {
-    // Done element by element inside AGPRs (read, multiply, write back) so
-    // that O never gets a VGPR copy the register allocator would have to
-    // keep.  The s_nops cover the MFMA-write -> accvgpr-read and
-    // accvgpr-write -> MFMA-read distances (this path is rare).
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4");
+  // O *= alpha.  The empty volatile asm keeps this a real (rarely taken)
+  // branch: the compiler would otherwise speculate the 64 multiplies into
+  // every step.
+  auto rescale = [&]() __attribute__((always_inline)) {
+    asm volatile("");
 #pragma unroll
     for (int md = 0; md < 4; ++md)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float t;
-        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                     : "+a"(oacc[md][nb][v]), "=&v"(t) : "v"(alpha[nb]));
-      }
-    asm volatile("s_nop 7");
+      for (int v = 0; v < 16; ++v) oacc[md][v] *= alpha;
   };
 
-  // One step j of a three-stage pipeline over 32-key sub-blocks: QK^T of
-  // sub-block j+2 (into Sn), PV of sub-block j (with P), softmax of
-  // sub-block j+1 (Sc -> Pn).  The three are independent; the MFMAs run as
-  // one phase and the softmax as another, in the order SOFT_FIRST gives (a
-  // scheduling barrier keeps the phases apart).  O is rescaled at the end
-  // of the step (after PV j, before PV j+1) if the softmax raised a running
-  // max.  MASK and SOFT_FIRST are compile-time.
+  // One step j of a three-stage pipeline over 32-key sub-blocks: P V of
+  // sub-block j (vf, P; the V^T operand was read in the previous step), Q K^T
+  // of sub-block j+2 (into Sn, K read from LDS in this step), the V^T operand
+  // of sub-block j+1 for the next step, and the softmax of sub-block j+1
+  // (Sc -> Pn).  O is rescaled at the end of the step (after P V j, before
+  // P V j+1) if the softmax raised the running max.
   // Sub-block x lives in ring slot (x / 2) % NSTAGE, half x % 2.
-  auto step = [&](auto mask_tag, int j, f32x16 (&Sc)[NB], f32x16 (&Sn)[NB],
-                  const bf16x8 (&P)[NB][2], bf16x8 (&Pn)[NB][2], auto order_tag) __attribute__((always_inline)) {
+  auto step = [&](auto mask_tag, int j, f32x16& Sc, f32x16& Sn, const bf16x8 (&P)[2],
+                  bf16x8 (&Pn)[2]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool SOFT_FIRST = decltype(order_tag)::value;
-    bf16x8 kf[8], vf[8];
+    if (WITH_O) pv(P);
+    bf16x8 kf[8];
     load_k(((j + 2) >> 1) % NSTAGE, j & 1, kf);
-    if (WITH_O) load_v((j >> 1) % NSTAGE, j & 1, vf);
-    if (!SOFT_FIRST) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) qk_half(kf, nb, Sn[nb]);
-      if (WITH_O) pv_mfma(vf, P);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const int kb_soft = k0 + 32 * (j + 1);
-    bool r[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      r[nb] = softmax_half(Sc[nb], MASK, kb_soft, nb, Pn[nb]);
-      // Pin the softmax results (P and the row sums) to this point so that
-      // their VALU work stays between this step's MFMAs; the s_nop keeps
-      // the last P write four wait states ahead of the PV MFMAs that read it.
-      asm volatile("s_nop 3" : "+v"(Pn[nb][0]), "+v"(Pn[nb][1]));
-      asm volatile("" : "+v"(lp[nb][0]), "+v"(lp[nb][1]), "+v"(lp[nb][2]), "+v"(lp[nb][3]));
-    }
-    if (SOFT_FIRST) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) qk_half(kf, nb, Sn[nb]);
-      if (WITH_O) pv_mfma(vf, P);
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      if (WITH_O && r[nb]) rescale_half(nb);
+    qk(kf, Sn);
+    if (WITH_O) load_v(((j + 1) >> 1) % NSTAGE, (j + 1) & 1, vf);
+    const bool r = softmax(Sc, MASK, k0 + 32 * (j + 1), Pn);
+    // The softmax results are used only in the next step; pinned here, they
+    // stay in this step's scheduling region instead of sinking below the
+    // rescale branch.
+    asm volatile("" : "+v"(Pn[0]), "+v"(Pn[1]));
+    asm volatile("" : "+v"(lp[0]), "+v"(lp[1]), "+v"(lp[2]), "+v"(lp[3]));
+    if (WITH_O && r) rescale();
   };
 
   const int n_sub = (k1 - k0 + 31) / 32;
@@ -645,155 +607,163 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
   constexpr int per_stage = WITH_O ? 2 * NCP : NCP;   // copies per wave per stage
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i) issue_stage(page_of_block(k0 + i * KB), i);
-  int pg_next = page_of_block(k0 + (NSTAGE - 1) * KB);
   // Q is loaded after the first stage copies are on their way (one wait
-  // covers both) and stays in AGPRs for the whole kernel (MFMA reads its B
-  // operand from there), leaving the VGPRs to the softmax and LDS operands.
+  // covers both).
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qf[nb][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qptr[nb] + kk * 16));
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+a"(qf[nb][kk]));
+  for (int kk = 0; kk < 8; ++kk)
+    qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qptr + kk * 16));
   vm_wait_barrier<(NSTAGE - 2) * per_stage>();   // stage 0 resident
-  // (The last stage's tail is zeroed once the stage is resident; the next
-  // barrier orders those writes before any read of its values.)
-  if (tail_partial && n_stage == 1) zero_tail(k0, 0);
-  // prologue: S of sub-blocks 0 (even) and 1 (odd), softmax of sub-block 0
-  f32x16 S_even[NB], S_odd[NB];
-  bf16x8 Pa[NB][2], Pb[NB][2];
+  lgkm_settled();
+  if (tail_partial && n_stage == 1) {
+    zero_tail(k0, 0);
+    lds_barrier();
+  }
+  // prologue: S of sub-blocks 0 (even) and 1 (odd), softmax of sub-block 0,
+  // V operand of sub-block 0
+  f32x16 S_even, S_odd;
+  bf16x8 Pa[2], Pb[2];
   {
     bf16x8 kf[8];
     load_k(0, 0, kf);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) qk_half(kf, nb, S_even[nb]);
+    qk(kf, S_even);
     load_k(0, 1, kf);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) qk_half(kf, nb, S_odd[nb]);
-    const bool mask0 = k0 + 31 > wave_pmin;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      if (softmax_half(S_even[nb], mask0, k0, nb, Pa[nb]) && WITH_O) rescale_half(nb);
+    qk(kf, S_odd);
+    softmax(S_even, k0 + 31 > wave_pmin, k0, Pa);   // O is still 0: no rescale
+    if (WITH_O) load_v(0, 0, vf);
   }
 
   // Iteration b = steps 2b (A) and 2b+1 (B), after a barrier that makes
   // stage b+1 resident and frees the slot of stage b-1:
-  //   step A: QK^T 2b+2 (stage b+1), PV 2b (stage b), softmax 2b+1
-  //   step B: QK^T 2b+3 (stage b+1), PV 2b+1 (stage b), softmax 2b+2
+  //   step A: PV 2b (stage b), QK^T 2b+2 (stage b+1), V of 2b+1, softmax 2b+1
+  //   step B: PV 2b+1 (stage b), QK^T 2b+3 (stage b+1), V of 2b+2, softmax 2b+2
   // The K half of stage b+3 is copied before step A, its V half before
   // step B.  Work past the item's last sub-block is harmless (QK^T results
   // unused, softmax fully masked since causal limits are clamped to the
   // item's last key, reads inside the ring) except PV, so the loop exits
   // right after the last PV.  Sub-blocks wholly below the tile's first query
   // row need no causal mask: iterations b < b_plain are unmasked (and never
-  // reach the exit).
+  // reach the exit).  The last stage's values past the item's end are
+  // zeroed once it is resident; its V is first read in step B, after a
+  // barrier that orders those writes.
   const int tile_pmin = it.pad0;
   const int n_plain_sub = max(0, (min(tile_pmin, kmax) - k0 + 1) / 32);
   const int b_plain = max(0, (n_plain_sub - 1) / 2);
+  // The page id of stage b+3 is loaded (scalar) just before the barrier of
+  // iteration b, whose wait covers its latency.
+  int pg_next = 0;
   auto barrier_copy_k = [&](int b) __attribute__((always_inline)) {
+    pg_next = page_of_block(k0 + (b + 3) * KB);
     vm_wait_barrier<per_stage>();             // stage b+1 resident, b+2 may be in flight
-    if (tail_partial && b + 1 == n_stage - 1) zero_tail(k0 + (b + 1) * KB, (b + 1) % NSTAGE);
+    lgkm_settled();
+    if (tail_partial && b + 1 == n_stage - 1) {
+      zero_tail(k0 + (b + 1) * KB, (b + 1) % NSTAGE);
+      lds_barrier();
+    }
     issue_k(pg_next, (b + 3) % NSTAGE);
   };
   auto copy_v = [&](int b) __attribute__((always_inline)) {
     issue_v(pg_next, (b + 3) % NSTAGE);
-    pg_next = page_of_block(k0 + (b + NSTAGE) * KB);
   };
-  auto run = [&](auto order) __attribute__((always_inline)) {
-    int b = 0;
-    for (; b < b_plain; ++b) {
-      barrier_copy_k(b);
-      step(std::false_type{}, 2 * b, S_odd, S_even, Pa, Pb, order);
-      copy_v(b);
-      step(std::false_type{}, 2 * b + 1, S_even, S_odd, Pb, Pa, order);
-    }
-    for (;; ++b) {
-      barrier_copy_k(b);
-      step(std::true_type{}, 2 * b, S_odd, S_even, Pa, Pb, order);
-      if (2 * b + 1 >= n_sub) break;
-      copy_v(b);
-      step(std::true_type{}, 2 * b + 1, S_even, S_odd, Pb, Pa, order);
-      if (2 * b + 2 >= n_sub) break;
-    }
-  };
-  // The two waves of a SIMD (w and w + 4) run each step's MFMAs and its
-  // softmax in opposite orders, so that one's VALU work tends to meet the
-  // other's MFMAs; each order is a separate copy of the loop.
-  if (NB == 1 && wu >= 4) run(std::true_type{}); else run(std::false_type{});
-  // No stage copy may still be writing LDS when the workgroup ends; the
-  // last PV MFMAs finish before O is read.
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
+  int b = 0;
+  for (; b < b_plain; ++b) {
+    barrier_copy_k(b);
+    step(std::false_type{}, 2 * b, S_odd, S_even, Pa, Pb);
+    copy_v(b);
+    step(std::false_type{}, 2 * b + 1, S_even, S_odd, Pb, Pa);
+  }
+  for (;; ++b) {
+    barrier_copy_k(b);
+    step(std::true_type{}, 2 * b, S_odd, S_even, Pa, Pb);
+    if (2 * b + 1 >= n_sub) break;
+    copy_v(b);
+    step(std::true_type{}, 2 * b + 1, S_even, S_odd, Pb, Pa);
+    if (2 * b + 2 >= n_sub) break;
+  }
+  // No stage copy may still be writing LDS when the workgroup ends.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue ----------------------------------------------------------------
   // Final outputs go through LDS (the stage ring is free once every wave's
-  // copies have landed): each wave writes its 32 NB normalised bf16 output
-  // rows of 256 bytes there, then stores whole rows, 16 lanes per row, so
-  // HBM sees full lines instead of 8-byte pieces of 32 rows per instruction.
-  // Rows are padded to 272 bytes so the row-strided writes spread over the
-  // banks.
+  // copies have landed): each wave writes its 32 normalised bf16 output rows
+  // of 256 bytes there, then stores whole rows, 16 lanes per row, so HBM sees
+  // full lines instead of 8-byte pieces of 32 rows per instruction.  Rows are
+  // padded to 272 bytes so the row-strided writes spread over the banks.
   constexpr int kStgLd = 136;
   static_assert(8 * 32 * kStgLd * 2 <= NSTAGE * (int)sizeof(Stage), "output staging fits the ring");
   const bool final_out = it.slot < 0;
-  uint16_t* stg = reinterpret_cast<uint16_t*>(smem_raw) + (size_t)w * (32 * NB) * kStgLd;
+  uint16_t* stg = reinterpret_cast<uint16_t*>(smem_raw) + (size_t)w * 32 * kStgLd;
   if (WITH_O && final_out) __syncthreads();
+  const bool valid = pair < npairs;
+  const int r = pair / G, hh = pair - r * G;
+  const int m = it.row0 + r;
+  const int h = g * G + hh;
+  const float l_tot = half_sum((lp[0] + lp[1]) + (lp[2] + lp[3]));
+  const float m2 = m_run * c;                         // log2-domain max
+  if (final_out) {
+    if (lse && valid && hl == 0) lse[(size_t)m * hq + h] = (m2 + __log2f(l_tot)) * kLn2;
+    if (WITH_O) {
+      const float inv = 1.f / l_tot;
+      uint16_t* sp = stg + (lane & 31) * kStgLd + 4 * hl;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int p = 32 * NB * w + 32 * nb + (lane & 31);
-    const bool valid = p < npairs;
-    const int r = p / G, hh = p - r * G;
-    const int m = it.row0 + r;
-    const int h = g * G + hh;
-    const float l_tot = half_sum((lp[nb][0] + lp[nb][1]) + (lp[nb][2] + lp[nb][3]));
-    const float m2 = m_run[nb] * c;                     // log2-domain max
-    if (it.slot < 0) {
-      if (lse && valid && hl == 0) lse[(size_t)m * hq + h] = (m2 + __log2f(l_tot)) * kLn2;
-      if (WITH_O) {
-        const float inv = 1.f / l_tot;
-        uint16_t* sp = stg + (32 * nb + (lane & 31)) * kStgLd + 4 * hl;
+      for (int md = 0; md < 4; ++md)
 #pragma unroll
-        for (int md = 0; md < 4; ++md)
+        for (int j = 0; j < 4; ++j) {
+          u32x2 pk;
+          pk[0] = pack_bf2(oacc[md][4 * j] * inv, oacc[md][4 * j + 1] * inv);
+          pk[1] = pack_bf2(oacc[md][4 * j + 2] * inv, oacc[md][4 * j + 3] * inv);
+          *reinterpret_cast<u32x2*>(sp + md * 32 + 8 * j) = pk;
+        }
+    }
+  } else if (it.slot < max_slots) {
+    // Split tile: the chunk's max, row sum and normalised output go to the
+    // partial slot.  The output is stored as fp16 scaled by 2^-e, with e the
+    // smallest power that brings the pair's largest |o| below 2^15 (0 for
+    // |o| < 2^15), so any value bf16 can hold survives; the merge multiplies
+    // by 2^e again.
+    const size_t pslot = ((size_t)it.slot * hkv + g) * PAIRS + pair;
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // a chunk past the row: o = 0
+    float scl = 1.f;
+    if (WITH_O) {
+      float amax = 0.f;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            u32x2 pk;
-            pk[0] = pack_bf2(oacc[md][nb][4 * j] * inv, oacc[md][nb][4 * j + 1] * inv);
-            pk[1] = pack_bf2(oacc[md][nb][4 * j + 2] * inv, oacc[md][nb][4 * j + 3] * inv);
-            *reinterpret_cast<u32x2*>(sp + md * 32 + 8 * j) = pk;
-          }
+      for (int md = 0; md < 4; ++md)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(oacc[md][v]));
+      amax = half_max(amax) * inv;
+      if (amax >= 32768.f && amax <= 3.0e38f) {
+        const int e = __builtin_amdgcn_frexp_expf(amax);       // amax = f 2^e, f in [0.5, 1)
+        scl = __builtin_ldexpf(1.f, e - 15);
+        inv = __builtin_ldexpf(inv, 15 - e);
       }
-    } else if (it.slot < max_slots) {
-      const size_t pslot = ((size_t)it.slot * hkv + g) * PAIRS + p;
-      if (hl == 0) {
-        part_ml[2 * pslot] = m2;
-        part_ml[2 * pslot + 1] = l_tot;
-      }
-      if (WITH_O) {                        // normalised partial output, fp16
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // a chunk past the row: o = 0
-        uint16_t* op = part_o + pslot * 128 + 4 * hl;
+    }
+    if (hl == 0) {
+      part_ml[4 * pslot] = m2;
+      part_ml[4 * pslot + 1] = l_tot;
+      part_ml[4 * pslot + 2] = scl;
+    }
+    if (WITH_O) {
+      uint16_t* op = part_o + pslot * 128 + 4 * hl;
 #pragma unroll
-        for (int md = 0; md < 4; ++md)
+      for (int md = 0; md < 4; ++md)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            u32x2 pk;
-            pk[0] = pack_h2(oacc[md][nb][4 * j] * inv, oacc[md][nb][4 * j + 1] * inv);
-            pk[1] = pack_h2(oacc[md][nb][4 * j + 2] * inv, oacc[md][nb][4 * j + 3] * inv);
-            *reinterpret_cast<u32x2*>(op + md * 32 + 8 * j) = pk;
-          }
-      }
+        for (int j = 0; j < 4; ++j) {
+          u32x2 pk;
+          pk[0] = pack_h2(oacc[md][4 * j] * inv, oacc[md][4 * j + 1] * inv);
+          pk[1] = pack_h2(oacc[md][4 * j + 2] * inv, oacc[md][4 * j + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + md * 32 + 8 * j) = pk;
+        }
     }
   }
   if (WITH_O && final_out) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's staging writes are done
 #pragma unroll
-    for (int i = 0; i < 8 * NB; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int pl = 4 * i + (lane >> 4), ch = lane & 15;
-      const int p = 32 * NB * w + pl;
-      if (p < npairs) {
-        const int r = p / G, hh = p - r * G;
+      const int pp = 32 * w + pl;
+      if (pp < npairs) {
+        const int rr = pp / G, hh2 = pp - rr * G;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stg + pl * kStgLd + ch * 8);
-        *reinterpret_cast<u32x4*>(o + ((size_t)(it.row0 + r) * hq + g * G + hh) * 128 + ch * 8) = v;
+        *reinterpret_cast<u32x4*>(o + ((size_t)(it.row0 + rr) * hq + g * G + hh2) * 128 + ch * 8) = v;
       }
     }
   }
@@ -803,8 +773,8 @@ __global__ __launch_bounds__(64 * (8 / NB), 1) void attn_fwd(
 //   M = max_c m_c,  w_c = l_c 2^(m_c - M),  O = sum_c w_c O_c / sum_c w_c,
 //   LSE = (M + log2 sum_c w_c) ln 2.
 // One workgroup per (merge tile, kv head, group of 16 pairs); 16 threads per
-// pair, 8 head dimensions per thread.  Partial outputs are fp16 (normalised,
-// so bounded by the largest value magnitude).
+// pair, 8 head dimensions per thread.  Partial outputs are normalised fp16
+// values times 2^-e; the slot's third float holds 2^e.
 constexpr int kMergePairs = 16;
 template <bool WITH_O>
 __global__ __launch_bounds__(256) void attn_merge(
@@ -825,21 +795,22 @@ __global__ __launch_bounds__(256) void attn_merge(
     float M = -INFINITY;
     for (int c = 0; c < mt.n_chunks; ++c) {
       const size_t ps = ((size_t)(mt.slot0 + c) * hkv + g) * PAIRS + p;
-      M = fmaxf(M, part_ml[2 * ps]);
+      M = fmaxf(M, part_ml[4 * ps]);
     }
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float wsum = 0.f;
     for (int c = 0; c < mt.n_chunks; ++c) {
       const size_t ps = ((size_t)(mt.slot0 + c) * hkv + g) * PAIRS + p;
-      const float wc = part_ml[2 * ps + 1] * __builtin_amdgcn_exp2f(part_ml[2 * ps] - M);
+      const float wc = part_ml[4 * ps + 1] * __builtin_amdgcn_exp2f(part_ml[4 * ps] - M);
       wsum += wc;
       if (WITH_O) {
+        const float wo = wc * part_ml[4 * ps + 2];
         const u32x4 raw = *reinterpret_cast<const u32x4*>(part_o + ps * 128 + sub * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const f32x2_t a = unpack_h2(raw[e]);
-          acc[2 * e] = fmaf(wc, a[0], acc[2 * e]);
-          acc[2 * e + 1] = fmaf(wc, a[1], acc[2 * e + 1]);
+          acc[2 * e] = fmaf(wo, a[0], acc[2 * e]);
+          acc[2 * e + 1] = fmaf(wo, a[1], acc[2 * e + 1]);
         }
       }
     }
@@ -945,10 +916,10 @@ sx_status run_bf16(const sx_dims& dims, const sx_layout& lay, const void* q,
   float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
   uint16_t* part_o = WITH_O ? reinterpret_cast<uint16_t*>(base + L.part_o) : nullptr;
   const size_t smem = NSTAGE * sizeof(Stage);
-  sx_status st = allow_lds((const void*)attn_fwd<WITH_O, kHalvesPerWave>, smem, "attention");
+  sx_status st = allow_lds((const void*)attn_fwd<WITH_O>, smem, "attention");
   if (st != SX_OK) return st;
   const float scale_log2 = kLog2e / sqrtf((float)dims.head_dim);
-  attn_fwd<WITH_O, kHalvesPerWave><<<L.max_items * hkv, 64 * (8 / kHalvesPerWave), smem, stream>>>(
+  attn_fwd<WITH_O><<<L.max_items * hkv, 512, smem, stream>>>(
       (const uint16_t*)q, q_index, rows, lay, kv.n_pages, (const uint16_t*)kv.k,
       (const uint16_t*)kv.v, hkv, G, (uint16_t*)o, lse, items, counters, part_ml, part_o,
       L.max_items, scale_log2);
