@@ -36,5 +36,4 @@ from .sparsex import (  # noqa: F401
     select_topk,
     sparse_layer,
     full_layer,
-    rms_norm,
 )

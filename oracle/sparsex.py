@@ -34,7 +34,6 @@ __all__ = [
     "select_topk",
     "sparse_layer",
     "full_layer",
-    "rms_norm",
 ]
 
 # ---------------------------------------------------------------------------
@@ -432,11 +431,3 @@ def full_layer(x, wq, wk, wv, theta: float, n_q_heads: int, n_kv_heads: int, hea
     O, lse = causal_attention(q, np.arange(T), k, v)
     O = O.reshape(T, n_q_heads * head_dim)
     return dict(O=round_store(O, dtype), O_exact=O, lse=lse, K=k, V=v, q=q)
-
-
-def rms_norm(x, eps: float) -> np.ndarray:
-    """RMSNorm with unit gain: x / sqrt(mean(x^2) + eps), per row (float64).
-
-    Stack glue between layers (not part of the paper's method)."""
-    x = np.asarray(x, dtype=np.float64)
-    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)

@@ -111,11 +111,16 @@ class SparseXLayerRun:
     """
 
     def __init__(self, case, device="cuda", ratios=None, extra_guard_pages: int = 8,
-                 overflow_tokens: int = 0):
+                 overflow_tokens: int = 0, keep_probe_cache: bool = False):
         import torch as _t
         from . import synth
         self.case = case
         self.device = device
+        # keep a device copy of the K pool as the selection read it (after the
+        # realignment and the Sparse-Q rows, before the selected rows are
+        # recomputed), for inspection
+        self.keep_probe_cache = keep_probe_cache
+        self.probe_k = None
         d = case.dims
         self.dims = d
         self.cdims = make_dims(d)
@@ -220,6 +225,8 @@ class SparseXLayerRun:
         ws = workspace(L.SX_OP_SELECT, cd, self.n_tok, n_sq, n_req, dev)
         L.sx_select_topk(cd, self.lay.struct, self.q_sq, None, sq_rows, sq_start, n_sq, None, pages,
                          tok_class, k_sel, self.sel_rows, self.act_rows, self.scores, ws)
+        if self.keep_probe_cache:
+            self.probe_k = self.pool.k.clone()
         act_start_h = (plan["sq_start"] + np.concatenate([[0], np.cumsum(k)])).astype(np.int32)
         self.act_start = torch.from_numpy(act_start_h).to(dev)
         self.q_act = torch.empty((n_act, d.n_q_heads, d.head_dim), dtype=self.dt, device=dev)
@@ -236,3 +243,15 @@ class SparseXLayerRun:
     def request_cache(self, r: int):
         T = int(self.plan["seq_start"][r + 1] - self.plan["seq_start"][r])
         return gather_logical(self.pool, self.block_table[r], T)
+
+    def probe_keys(self, r: int):
+        """Request r's keys as the selection read them ([T, Hkv, d], host);
+        needs keep_probe_cache."""
+        T = int(self.plan["seq_start"][r + 1] - self.plan["seq_start"][r])
+        k, _ = gather_logical(PagePool(self.probe_k, self.pool.v), self.block_table[r], T)
+        return k
+
+    def sq_queries(self, r: int):
+        """Request r's Sparse-Q query rows as stored ([n_sq_r, Hq, d], host)."""
+        a, b = int(self.plan["sq_start"][r]), int(self.plan["sq_start"][r + 1])
+        return self.q_sq[a:b].float().cpu().double().numpy()

@@ -31,8 +31,13 @@ class HybridStackRun:
     """
 
     def __init__(self, dims, n_layers: int, threshold: int, layout, seg_len, seg_p_src, ratios,
-                 inputs, device="cuda", page_seed: int = 7, overflow_tokens: int = 0):
+                 inputs, device="cuda", page_seed: int = 7, overflow_tokens: int = 0,
+                 keep_probe_cache: bool = False):
         self.dims, self.cdims = dims, make_dims(dims)
+        # threshold 0: keep a device copy of layer 0's K pool as the in-layer
+        # probe read it (before the selected rows are recomputed)
+        self.keep_probe_cache = keep_probe_cache
+        self.probe_k = None
         self.n_layers, self.t = n_layers, threshold
         self.device = device
         self.dt = storage_dtype(dims.dtype)
@@ -173,6 +178,8 @@ class HybridStackRun:
             L.sx_select_topk(self.cdims, self.lay.struct, self.q_full, None, self.sq_rows, self.sq_start,
                              self.n_sq, None, pages, self.tok_class, self.k_sel, self.sel_rows,
                              self.act_rows, self.scores, self.ws_sel)
+        if self.keep_probe_cache:
+            self.probe_k = self.req_pools[l].k.clone()
 
     def sparse_prep(self, l: int, timer=None, realign: bool = True):
         """Layer l's cache and queries: realign its reused runs, recompute A."""

@@ -105,3 +105,68 @@ def selection_contract(gpu_sel, ora_scores, cand, k, tol):
         near = np.abs(ora_scores[diff] - kth) <= 2 * tol
         assert near.all(), "selection differs outside the near-tie band"
     return len(diff)
+
+
+O_STRICT_LIMIT = 2.56   # below this |r|, a bf16 store's half step is under 1e-2
+
+
+def assert_o_bf16(got, ref, what=""):
+    """Layer output against the unrounded oracle: max |g - r| <= 1e-2 wherever
+    |r| < 2.56 (the bound the output contract states; a bf16 store of such a
+    value is off by at most 2^-8 |r| < 1e-2), and 1e-2 + 2^-8 |r| for larger
+    |r|, where the store alone can exceed 1e-2.  Returns the max abs error."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = np.abs(got - ref)
+    small = np.abs(ref) < O_STRICT_LIMIT
+    tol = np.where(small, 1e-2, 1e-2 + BF16_HALF_STEP_REL * np.abs(ref))
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; "
+                           f"max err {err.max():.3g} at {np.unravel_index(err.argmax(), err.shape)}")
+    return float(err.max())
+
+
+SCORE_REL_TOL = 1e-5    # GPU scores vs oracle scores from the GPU's own Q and K
+
+
+def check_selection(gpu_scores, gpu_sel, ref_scores, cand, k, what=""):
+    """Index parity of the Sparse-Q selection.
+
+    ref_scores are the oracle's attention-mass scores computed from the
+    query and key values the GPU stored (so storage rounding is not part of
+    the comparison).  Checks, in order:
+      1. the GPU's selection is exactly the top-k of the GPU's own scores
+         (score descending, lower index first);
+      2. every score is within 1e-5 * max(ref) of the oracle's;
+      3. the selection equals the oracle's top-k on ref_scores, except for
+         indices whose oracle score lies within 2 * tol of the k-th one,
+         where scores equal within tolerance may order either way; with a
+         k-th/(k+1)-th margin above 2 * tol there may be no difference.
+    Returns (number of differing indices, max score error / max ref)."""
+    import oracle
+    gpu_scores = np.asarray(gpu_scores, dtype=np.float64)
+    ref_scores = np.asarray(ref_scores, dtype=np.float64)
+    cand = np.asarray(cand, dtype=np.int64)
+    got = np.sort(np.asarray(gpu_sel, dtype=np.int64))
+    assert np.array_equal(got, oracle.select_topk(gpu_scores, cand, k)), \
+        f"{what}: selection is not the top-k of the GPU's own scores"
+    smax = float(np.max(ref_scores[cand])) if len(cand) else 0.0
+    tol = SCORE_REL_TOL * max(smax, 1e-30)
+    err = float(np.max(np.abs(gpu_scores[cand] - ref_scores[cand]))) if len(cand) else 0.0
+    assert err <= tol, f"{what}: score error {err:.3g} > {SCORE_REL_TOL} * max {smax:.3g}"
+    nd = selection_contract(got, ref_scores, cand, k, tol)
+    if 0 < k < len(cand):
+        s = np.sort(ref_scores[cand])[::-1]
+        band = int(np.sum(np.abs(ref_scores[cand] - s[k - 1]) <= 2 * tol))
+        assert nd <= 2 * band, f"{what}: {nd} differences for {band} candidates in the near-tie band"
+    return nd, err / max(smax, 1e-30)
+
+
+def probe_lse_and_scores(q_sq, sq_pos, K):
+    """Oracle LSE and attention-mass scores of the Sparse-Q rows from given
+    (GPU-stored) queries and keys."""
+    import oracle
+    _, lse = oracle.causal_attention(q_sq, sq_pos, K, K)
+    return lse, oracle.attention_mass_scores(q_sq, sq_pos, K, lse)
