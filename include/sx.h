@@ -17,7 +17,8 @@
  * - Pointers are DEVICE pointers unless the parameter name ends in `_h`
  *   (host memory).  The caller owns every buffer; the library allocates and
  *   frees nothing and keeps no state between calls -- except the segment
- *   index (sx_index_*), a host object the caller creates and destroys.
+ *   index (sx_index_*), a host object the caller creates and destroys, and
+ *   the static scratch array of sx_decode_attn_noalloc.
  * - Every compute call enqueues its kernels on `stream` (a hipStream_t; NULL
  *   is the null stream) and returns without synchronising.  Results are
  *   valid in stream order.
@@ -398,6 +399,24 @@ sx_status sx_full_attn(const sx_dims *dims, const sx_layout *lay, const void *q,
 sx_status sx_decode_attn(const sx_dims *dims, const sx_layout *lay, const void *q,
                          const sx_pages *kv, void *o, float *lse, void *ws, size_t ws_bytes,
                          void *stream);
+
+/* sx_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory around the call: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The partial results
+ * go to a static scratch array of SX_DECODE_NOALLOC_SCRATCH_BYTES (4 MiB)
+ * inside the library; each GPU holds its own copy until the process ends.
+ * The first call on a device looks up that device's copy (the stream must
+ * belong to the current device).  Calls whose workspace need
+ * (sx_workspace_bytes(SX_OP_DECODE, ...)) exceeds the scratch return
+ * SX_EWORKSPACE and launch nothing; with Llama-3-8B shapes that is above
+ * about 250 requests per call.  Every call on one GPU shares its scratch, so
+ * calls that overlap on one GPU (different streams without ordering, or
+ * different host threads) race and give wrong results.  The call allocates
+ * and frees nothing.  Arguments, outputs and other errors as for
+ * sx_decode_attn; the results are bitwise those of sx_decode_attn. */
+#define SX_DECODE_NOALLOC_SCRATCH_BYTES (4u << 20)
+sx_status sx_decode_attn_noalloc(const sx_dims *dims, const sx_layout *lay, const void *q,
+                                 const sx_pages *kv, void *o, float *lse, void *stream);
 
 /* Measurement utility, not a step of the method: a throughput probe of the
  * MFMA units, the measured counterpart of the data-sheet bf16 peak that the

@@ -23,7 +23,7 @@ SX_OP_REALIGN, SX_OP_RECOMPUTE, SX_OP_SELECT, SX_OP_TOPK, SX_OP_SPARSE_ATTN, SX_
 EXPORTED = [
     "sx_rope_table", "sx_plan_layout", "sx_plan_realign", "sx_realign_jobs_bound",
     "sx_workspace_bytes", "sx_rope_realign", "sx_recompute_kv", "sx_select_topk", "sx_topk",
-    "sx_sparse_attn", "sx_sparse_attn_plan", "sx_sparse_attn_run", "sx_full_attn", "sx_decode_attn", "sx_mfma_peak_probe", "sx_last_error",
+    "sx_sparse_attn", "sx_sparse_attn_plan", "sx_sparse_attn_run", "sx_full_attn", "sx_decode_attn", "sx_decode_attn_noalloc", "sx_mfma_peak_probe", "sx_last_error",
     "sx_virtual_hash", "sx_index_create", "sx_index_destroy", "sx_index_alloc", "sx_index_release",
     "sx_index_insert", "sx_index_lookup", "sx_index_remove", "sx_index_stats", "sx_plan_segments",
 ]
@@ -87,6 +87,7 @@ def lib():
             "sx_sparse_attn_run": (I, [P, P, P, P, I, P, P, P, P, Z, P]),
             "sx_full_attn": (I, [P, P, P, P, P, P, P, Z, P]),
             "sx_decode_attn": (I, [P, P, P, P, P, P, P, Z, P]),
+            "sx_decode_attn_noalloc": (I, [P, P, P, P, P, P, P]),
             "sx_mfma_peak_probe": (I, [I, I, P, P]),
             "sx_last_error": (C.c_char_p, []),
             "sx_virtual_hash": (I, [P, I, U, P]),
@@ -347,6 +348,11 @@ def sx_decode_attn(dims: Dims, lay: Layout, q, kv: Pages, o, lse, ws, stream=Non
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().sx_decode_attn(_ref(dims), _ref(lay), _ptr(q), _ref(kv), _ptr(o), _ptr(lse),
                                 _ptr(ws), ws_bytes, _stream(stream)), "sx_decode_attn")
+
+
+def sx_decode_attn_noalloc(dims: Dims, lay: Layout, q, kv: Pages, o, lse, stream=None):
+    _check(lib().sx_decode_attn_noalloc(_ref(dims), _ref(lay), _ptr(q), _ref(kv), _ptr(o),
+                                        _ptr(lse), _stream(stream)), "sx_decode_attn_noalloc")
 
 
 def sx_mfma_peak_probe(n_workgroups: int, iters: int, out, stream=None):

@@ -367,6 +367,24 @@ sx_status sx_decode_attn(const sx_dims* dims, const sx_layout* lay, const void* 
   return launch_decode(*dims, *lay, q, *kv, o, lse, ws, as_stream(stream));
 }
 
+sx_status sx_decode_attn_noalloc(const sx_dims* dims, const sx_layout* lay, const void* q,
+                                 const sx_pages* kv, void* o, float* lse, void* stream) {
+  const char* fn = "sx_decode_attn_noalloc";
+  SX_TRY(check_dims(dims, fn));
+  SX_REQUIRE(dims->dtype == SX_BF16, SX_EUNSUPPORTED, "%s: only the bf16 path is built", fn);
+  SX_TRY(check_layout(lay, fn));
+  SX_TRY(check_pages(kv, fn, "kv"));
+  SX_REQUIRE(q && o, SX_EINVAL, "%s: q/o is NULL", fn);
+  const size_t need = sx_workspace_bytes(SX_OP_DECODE, dims, lay->n_tok, 0, lay->n_req);
+  SX_REQUIRE(need <= decode_noalloc_capacity(), SX_EWORKSPACE,
+             "%s: this batch needs %zu bytes of scratch, the static scratch holds %zu "
+             "(split the batch, or use sx_decode_attn with a workspace)",
+             fn, need, decode_noalloc_capacity());
+  void* ws = nullptr;
+  SX_TRY(decode_scratch(&ws));
+  return launch_decode(*dims, *lay, q, *kv, o, lse, ws, as_stream(stream));
+}
+
 sx_status sx_mfma_peak_probe(int32_t n_workgroups, int32_t iters, float* out, void* stream) {
   const char* fn = "sx_mfma_peak_probe";
   SX_REQUIRE(n_workgroups >= 1 && n_workgroups <= (1 << 20), SX_EINVAL, "%s: n_workgroups must be in [1, 2^20]", fn);

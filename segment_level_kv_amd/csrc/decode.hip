@@ -24,11 +24,25 @@
 //   - online softmax in the log2 domain per wave; the 4 waves are merged in
 //     LDS; one fp32 partial (m, l, o) per (request, head, slot) goes to the
 //     workspace and decode_merge combines the slots in a fixed order.
+#include <mutex>
+
 #include "sx_device.hpp"
 #include "sx_internal.hpp"
 
 namespace sx {
 namespace {
+
+// Scratch of sx_decode_attn_noalloc: the partial results of decode_fwd live
+// in this file-scope array instead of a caller workspace.  Every GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// the name `scratch` is only a stand-in; the device address of this GPU's
+// copy comes from hipGetSymbolAddress (decode_scratch below) and is the only
+// thing passed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
@@ -344,6 +358,28 @@ int decode_slots(const sx_dims& d, int n_tok, int n_req) {
   const int cap = (n_tok + 4 * kUnitKeys - 1) / (4 * kUnitKeys);   // >= 1 unit per wave
   if (s > cap) s = cap;
   return s < 1 ? 1 : s;
+}
+
+size_t decode_noalloc_capacity() { return kNoAllocScratchBytes; }
+
+// This device's copy of `scratch`, looked up once per device (with that
+// device current) and kept.
+sx_status decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(SX_EDEVICE, "decode scratch: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(SX_EUNSUPPORTED, "decode scratch: device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(SX_EDEVICE, "decode scratch: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return SX_OK;
 }
 
 size_t decode_ws_bytes(const sx_dims& d, int n_tok, int n_req) {

@@ -57,6 +57,10 @@ sx_status launch_attention_run(const sx_dims& dims, const sx_layout& lay, const 
 size_t decode_ws_bytes(const sx_dims& d, int n_tok, int n_req);
 sx_status launch_decode(const sx_dims& dims, const sx_layout& lay, const void* q, const sx_pages& kv,
                         void* o, float* lse, void* ws, hipStream_t stream);
+// The static scratch of sx_decode_attn_noalloc: its size, and the current
+// device's address of it (looked up on the first call per device).
+size_t decode_noalloc_capacity();
+sx_status decode_scratch(void** ptr);
 
 // Partial score rows the score pass writes ([parts][n_tok]): one per kv head,
 // or per query head for bf16 prompts too short to fill the chip with kv-head
