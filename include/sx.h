@@ -25,10 +25,28 @@
  * - Scalars and host arrays are validated before anything is launched; on
  *   a bad argument the call returns a negative sx_status, launches nothing
  *   and sx_last_error() describes the problem.  Device-resident index data
- *   (block tables, row lists, page ids) is not inspected on the host; the
- *   kernels bound-check every index they dereference and skip an access
- *   that would fall outside the buffer it indexes (the result is then
- *   unspecified, but no memory outside the caller's buffers is touched).
+ *   (request offsets, block tables, row lists, realign jobs) is not
+ *   inspected on the host.  The kernels bound-check every index they
+ *   dereference, so bad index data never makes them touch memory outside
+ *   the buffers the call was given; instead: a page id outside [0, n_pages)
+ *   reads page 0 and its writes are skipped; a realign job whose pages,
+ *   slots, count or |delta| (>= rope_len) are out of range is skipped, its
+ *   destination slots keeping their old contents; a RoPE position outside
+ *   the table is clamped into it; a row that is not a token of the batch
+ *   reads row 0 of x and writes nothing; a row outside its request or out
+ *   of order is clamped to the request's keys.  The outputs that depend on
+ *   a bad index are then unspecified.
+ * - Debug mode: with the environment variable SX_DEBUG set (to anything but
+ *   "0") every device entry point except sx_topk first runs device-side
+ *   checks of the index data it will read -- request offsets (ascending,
+ *   from 0 to n_tok), the block-table page ids of every request's tokens
+ *   (in [0, n_pages), within max_pages columns), RoPE positions
+ *   (sx_recompute_kv: in [0, rope_len)), row lists (tokens of the batch;
+ *   where rows are grouped by request: ascending inside their request) and
+ *   realign jobs (pages, slots, counts, |delta| < rope_len).  If any check
+ *   fails the call returns SX_EDEVICE, sx_last_error() names what failed,
+ *   and none of its compute kernels is launched.  Debug mode waits for the
+ *   stream inside the call (it cannot be captured into a graph).
  * - Storage type: all of x, weights, Q, K/V pages and outputs of one call
  *   share `dims->dtype` (bf16 or fp32).  Accumulation is fp32.  Results
  *   are bitwise reproducible: reductions run in a fixed order, with no

@@ -30,7 +30,7 @@ CFLAGS = [
     "-Wall", "-Wno-unused-result",
 ]
 SOURCES = ["api.cpp", "seg_index.cpp", "rope_realign.hip", "recompute_kv.hip", "attention.hip",
-           "select.hip", "decode.hip", "mfma_peak.hip"]
+           "select.hip", "decode.hip", "mfma_peak.hip", "debug.hip"]
 # Per-source extra flags.  The attention softmax never produces NaN (masked
 # logits are -inf), so max reductions need no NaN quieting.  Compiler-selected
 # MFMAs in attention and in the selection's score pass write VGPRs (the score

@@ -77,6 +77,8 @@ sx_status check_layout(const sx_layout* L, const char* fn) {
   SX_REQUIRE(L->n_req >= 1 && L->n_req <= kMaxReq, SX_EINVAL, "%s: n_req must be in [1, %d]", fn, kMaxReq);
   SX_REQUIRE(L->n_tok >= 0, SX_EINVAL, "%s: n_tok must be >= 0", fn);
   SX_REQUIRE(L->max_pages >= 0, SX_EINVAL, "%s: max_pages must be >= 0", fn);
+  SX_REQUIRE(L->n_tok == 0 || L->max_pages > 0, SX_EINVAL,
+             "%s: max_pages is 0 but the batch has %d tokens", fn, L->n_tok);
   SX_REQUIRE(L->seq_start && L->block_table, SX_EINVAL, "%s: seq_start/block_table is NULL", fn);
   SX_REQUIRE(L->rope_tab && L->rope_len > 0, SX_EINVAL, "%s: rope_tab missing", fn);
   return SX_OK;
@@ -273,6 +275,11 @@ sx_status sx_rope_realign(const sx_dims* dims, const sx_layout* lay, const sx_pa
   SX_TRY(check_pages(dst, fn, "dst"));
   SX_REQUIRE(n_jobs >= 0, SX_EINVAL, "%s: n_jobs < 0", fn);
   SX_REQUIRE(n_jobs == 0 || jobs, SX_EINVAL, "%s: jobs is NULL", fn);
+  if (debug_enabled() && n_jobs > 0) {
+    DebugCheck dc(as_stream(stream), fn);
+    dc.jobs(jobs, n_jobs, src->n_pages, dst->n_pages, lay->rope_len);
+    SX_TRY(dc.finish());
+  }
   return launch_realign(*dims, *lay, *src, *dst, jobs, n_jobs, as_stream(stream));
 }
 
@@ -285,6 +292,12 @@ sx_status sx_recompute_kv(const sx_dims* dims, const sx_layout* lay, const void*
   SX_TRY(check_pages(kv, fn, "kv"));
   SX_REQUIRE(n_rows >= 0, SX_EINVAL, "%s: n_rows < 0", fn);
   SX_REQUIRE(n_rows == 0 || (x && rows && w_qkv), SX_EINVAL, "%s: x/rows/w_qkv is NULL", fn);
+  if (debug_enabled() && n_rows > 0) {
+    DebugCheck dc(as_stream(stream), fn);
+    dc.layout(*lay, kv->n_pages, true);
+    dc.rows(rows, nullptr, n_rows, *lay);
+    SX_TRY(dc.finish());
+  }
   return launch_recompute(*dims, *lay, x, rows, n_rows, w_qkv, *kv, q_out, as_stream(stream));
 }
 
@@ -302,6 +315,12 @@ sx_status sx_sparse_attn(const sx_dims* dims, const sx_layout* lay, const void* 
   const size_t need = sx_workspace_bytes(SX_OP_SPARSE_ATTN, dims, lay->n_tok, n_rows, lay->n_req);
   SX_REQUIRE(need == 0 || (ws && ws_bytes >= need), SX_EWORKSPACE,
              "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : (size_t)0);
+  if (debug_enabled()) {
+    DebugCheck dc(as_stream(stream), fn);
+    dc.layout(*lay, kv->n_pages, false);
+    dc.rows(rows, row_start, n_rows, *lay);
+    SX_TRY(dc.finish());
+  }
   return launch_attention(*dims, *lay, q, nullptr, rows, row_start, n_rows, *kv, o, lse, ws,
                           as_stream(stream));
 }
@@ -318,6 +337,12 @@ sx_status sx_sparse_attn_plan(const sx_dims* dims, const sx_layout* lay, const i
   const size_t need = sx_workspace_bytes(SX_OP_SPARSE_ATTN, dims, lay->n_tok, n_rows, lay->n_req);
   SX_REQUIRE(need == 0 || (ws && ws_bytes >= need), SX_EWORKSPACE,
              "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : (size_t)0);
+  if (debug_enabled()) {
+    DebugCheck dc(as_stream(stream), fn);
+    dc.layout(*lay, 1 << 30, false);   // the plan reads offsets and rows, not pages
+    dc.rows(rows, row_start, n_rows, *lay);
+    SX_TRY(dc.finish());
+  }
   return launch_attention_plan(*dims, *lay, rows, row_start, n_rows, ws, as_stream(stream));
 }
 
@@ -334,6 +359,12 @@ sx_status sx_sparse_attn_run(const sx_dims* dims, const sx_layout* lay, const vo
   const size_t need = sx_workspace_bytes(SX_OP_SPARSE_ATTN, dims, lay->n_tok, n_rows, lay->n_req);
   SX_REQUIRE(need == 0 || (ws && ws_bytes >= need), SX_EWORKSPACE,
              "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : (size_t)0);
+  if (debug_enabled()) {
+    DebugCheck dc(as_stream(stream), fn);
+    dc.layout(*lay, kv->n_pages, false);
+    dc.rows(rows, nullptr, n_rows, *lay);
+    SX_TRY(dc.finish());
+  }
   return launch_attention_run(*dims, *lay, q, nullptr, rows, n_rows, *kv, o, lse, ws, as_stream(stream));
 }
 
@@ -348,6 +379,11 @@ sx_status sx_full_attn(const sx_dims* dims, const sx_layout* lay, const void* q,
   const size_t need = sx_workspace_bytes(SX_OP_FULL_ATTN, dims, lay->n_tok, lay->n_tok, lay->n_req);
   SX_REQUIRE(need == 0 || (ws && ws_bytes >= need), SX_EWORKSPACE,
              "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : (size_t)0);
+  if (debug_enabled()) {
+    DebugCheck dc(as_stream(stream), fn);
+    dc.layout(*lay, kv->n_pages, false);
+    SX_TRY(dc.finish());
+  }
   return launch_attention(*dims, *lay, q, nullptr, nullptr, lay->seq_start, lay->n_tok, *kv, o, lse,
                           ws, as_stream(stream));
 }
@@ -364,6 +400,11 @@ sx_status sx_decode_attn(const sx_dims* dims, const sx_layout* lay, const void* 
   const size_t need = sx_workspace_bytes(SX_OP_DECODE, dims, lay->n_tok, 0, lay->n_req);
   SX_REQUIRE(ws && ws_bytes >= need, SX_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn,
              need, ws ? ws_bytes : (size_t)0);
+  if (debug_enabled()) {
+    DebugCheck dc(as_stream(stream), fn);
+    dc.layout(*lay, kv->n_pages, false);
+    SX_TRY(dc.finish());
+  }
   return launch_decode(*dims, *lay, q, *kv, o, lse, ws, as_stream(stream));
 }
 
@@ -380,6 +421,11 @@ sx_status sx_decode_attn_noalloc(const sx_dims* dims, const sx_layout* lay, cons
              "%s: this batch needs %zu bytes of scratch, the static scratch holds %zu "
              "(split the batch, or use sx_decode_attn with a workspace)",
              fn, need, decode_noalloc_capacity());
+  if (debug_enabled()) {
+    DebugCheck dc(as_stream(stream), fn);
+    dc.layout(*lay, kv->n_pages, false);
+    SX_TRY(dc.finish());
+  }
   void* ws = nullptr;
   SX_TRY(decode_scratch(&ws));
   return launch_decode(*dims, *lay, q, *kv, o, lse, ws, as_stream(stream));
@@ -423,6 +469,12 @@ sx_status sx_select_topk(const sx_dims* dims, const sx_layout* lay, const void* 
   SX_REQUIRE(ws && ws_bytes >= need, SX_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn,
              need, ws ? ws_bytes : (size_t)0);
   hipStream_t s = as_stream(stream);
+  if (debug_enabled()) {
+    DebugCheck dc(s, fn);
+    dc.layout(*lay, kv->n_pages, false);
+    dc.rows(sq_rows, sq_start, n_sq, *lay);
+    SX_TRY(dc.finish());
+  }
   char* p = static_cast<char*>(ws);
   float* partial = reinterpret_cast<float*>(p);
   p += align256((size_t)score_parts(*dims, lay->n_tok, lay->n_req) * lay->n_tok * sizeof(float));

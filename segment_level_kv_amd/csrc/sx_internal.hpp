@@ -79,6 +79,31 @@ sx_status launch_topk(const float* partial, int n_parts, const uint8_t* tok_clas
                       const int32_t* sq_start, int32_t* sel_rows, int32_t* act_rows,
                       float* scores_out, void* ws, hipStream_t stream);
 
+// SX_DEBUG device-side index checks (debug.hip).  debug_enabled(): the
+// environment variable SX_DEBUG is set to anything but "0".  A DebugCheck
+// clears its flag word on `stream`, each check enqueues a kernel that reads
+// the index data and ORs flags in, and finish() waits for the stream and
+// returns SX_EDEVICE (with the text in sx_last_error) if a flag is set.
+bool debug_enabled();
+class DebugCheck {
+ public:
+  DebugCheck(hipStream_t stream, const char* fn);
+  // request offsets and the block-table columns each request's tokens use;
+  // positions: also the RoPE positions of every token
+  void layout(const sx_layout& lay, int n_pages, bool positions);
+  // row_start != NULL: rows grouped by request, ascending inside it;
+  // row_start == NULL: every row a token of the batch
+  void rows(const int32_t* rows, const int32_t* row_start, int n_rows, const sx_layout& lay);
+  void jobs(const sx_realign_job* jobs, int n_jobs, int n_src_pages, int n_dst_pages, int rope_len);
+  sx_status finish();
+
+ private:
+  hipStream_t stream_;
+  const char* fn_;
+  int* flag_ = nullptr;
+  sx_status status_ = SX_OK;
+};
+
 // Back-to-back bf16 MFMAs on every compute unit (measured-peak probe).
 sx_status launch_mfma_peak(int n_workgroups, int iters, float* out, hipStream_t stream);
 

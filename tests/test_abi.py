@@ -94,6 +94,13 @@ def test_validation_errors_launch_nothing():
     assert lib.sx_mfma_peak_probe(4, 0, FAKE, None) == L.SX_EINVAL
     assert lib.sx_mfma_peak_probe(4, 10, None, None) == L.SX_EINVAL
     assert "sx_mfma_peak_probe" in L.last_error()
+    # a layout with tokens but no block-table columns
+    empty_bt = L.Layout(1, 16, 0, 16, 0x1000, 0x1000, None, 0x1000)
+    assert lib.sx_full_attn(C.byref(d), C.byref(empty_bt), FAKE, C.byref(pages), FAKE, None, FAKE,
+                            1 << 20, None) == L.SX_EINVAL
+    assert "max_pages" in L.last_error()
+    assert lib.sx_decode_attn_noalloc(C.byref(d), C.byref(empty_bt), FAKE, C.byref(pages), FAKE, None,
+                                      None) == L.SX_EINVAL
 
 
 def test_zero_sized_calls_are_noops():

@@ -1,0 +1,143 @@
+"""SX_DEBUG: device-side checks of the index data (GPU).
+
+The request offsets, block table (the paper's §4.5 scheduler output), row
+lists and realign jobs live on the device.  With SX_DEBUG=1 every device
+entry point checks them on the device before its compute kernels; a bad
+index makes the call return SX_EDEVICE, name the problem, and launch none of
+its compute kernels (outputs and page pools are left as they were).  Valid
+calls give the same bits with and without the checks.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from segment_level_kv_amd import _lib as L
+from segment_level_kv_amd import layer as LY
+from segment_level_kv_amd import synth
+from tests.gpu_util import say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+D = synth.Dims(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, theta=1e4, dtype="bf16")
+T = 100
+
+
+def _setup(seed=3, bad_page=False):
+    rng = np.random.default_rng(seed)
+    np_req = (T + 15) // 16
+    n_pages = 2 * np_req + 4
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    pool = LY.PagePool.alloc(n_pages, D, DEV, fill_guard=False)
+    pool.k.copy_(torch.randn(pool.k.shape, generator=g, device=DEV).to(torch.bfloat16))
+    pool.v.copy_(torch.randn(pool.v.shape, generator=g, device=DEV).to(torch.bfloat16))
+    perm = rng.permutation(n_pages).astype(np.int32)
+    bt = perm[:np_req][None, :].copy()
+    if bad_page:
+        bt[0, 3] = n_pages + 7
+    rope = LY.rope_table(D.theta, D.head_dim, T + 16, DEV)
+    lay = LY.DeviceLayout(np.array([0, T], np.int32), bt, rope, DEV)
+    return pool, bt, lay, perm
+
+
+def _expect_edevice(what, fn, *args):
+    with pytest.raises(L.SxError) as e:
+        fn(*args)
+    assert e.value.status == L.SX_EDEVICE, (what, e.value.status)
+    assert what in str(e.value), (what, str(e.value))
+    say(f"  {fn.__name__}: {str(e.value).split(': ', 1)[-1]}")
+
+
+def _attn_inputs(rows_h):
+    rows = torch.from_numpy(np.asarray(rows_h, np.int32)).to(DEV)
+    rs = torch.tensor([0, len(rows_h)], dtype=torch.int32, device=DEV)
+    q = torch.randn((len(rows_h), D.n_q_heads, D.head_dim), device=DEV).to(torch.bfloat16)
+    o = torch.full((len(rows_h), D.n_q_heads * D.head_dim), 5.0, dtype=torch.bfloat16, device=DEV)
+    return rows, rs, q, o
+
+
+def test_debug_valid_calls_give_the_same_bits(monkeypatch):
+    pool, bt, lay, _ = _setup()
+    cd = LY.make_dims(D)
+    rows_h = np.array([0, 5, 40, 63, 64, 99], np.int32)
+    rows, rs, q, _ = _attn_inputs(rows_h)
+    ws = LY.workspace(L.SX_OP_SPARSE_ATTN, cd, T, len(rows_h), 1, DEV)
+    outs = []
+    for dbg in ("0", "1"):
+        monkeypatch.setenv("SX_DEBUG", dbg)
+        o = torch.zeros((len(rows_h), D.n_q_heads * D.head_dim), dtype=torch.bfloat16, device=DEV)
+        L.sx_sparse_attn(cd, lay.struct, q, rows, rs, len(rows_h), pool.struct(), o, None, ws)
+        torch.cuda.synchronize()
+        outs.append(o)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+def test_debug_reports_bad_realign_jobs(monkeypatch):
+    monkeypatch.setenv("SX_DEBUG", "1")
+    pool, bt, lay, perm = _setup()
+    cd = LY.make_dims(D)
+    n_pages = pool.n_pages
+    before_k, before_v = pool.k.clone(), pool.v.clone()
+    src, dst = int(perm[-1]), int(bt[0, 0])
+    for job, what in [((src, n_pages + 3, 0, 0, 16, 4), "realign job"),
+                      ((src, dst, 0, 0, 16, T + 16 + 5), "realign delta"),
+                      ((src, dst, 8, 0, 16, 4), "realign job")]:
+        jobs = torch.tensor([job], dtype=torch.int32, device=DEV)
+        say(f"[debug] realign job {job}")
+        _expect_edevice(what, L.sx_rope_realign, cd, lay.struct, pool.struct(), pool.struct(), jobs, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(pool.k.view(torch.int16), before_k.view(torch.int16))
+    assert torch.equal(pool.v.view(torch.int16), before_v.view(torch.int16))
+
+
+def test_debug_reports_bad_block_table(monkeypatch):
+    monkeypatch.setenv("SX_DEBUG", "1")
+    pool, bt, lay, _ = _setup(bad_page=True)
+    cd = LY.make_dims(D)
+    rows_h = np.array([1, 30, 90], np.int32)
+    rows, rs, q, o = _attn_inputs(rows_h)
+    ws = LY.workspace(L.SX_OP_SPARSE_ATTN, cd, T, len(rows_h), 1, DEV)
+    say("[debug] page id past the pool in the block table")
+    _expect_edevice("block-table page id", L.sx_sparse_attn, cd, lay.struct, q, rows, rs, len(rows_h),
+                    pool.struct(), o, None, ws)
+    qf = torch.randn((T, D.n_q_heads, D.head_dim), device=DEV).to(torch.bfloat16)
+    of = torch.full((T, D.n_q_heads * D.head_dim), 5.0, dtype=torch.bfloat16, device=DEV)
+    wsf = LY.workspace(L.SX_OP_FULL_ATTN, cd, T, T, 1, DEV)
+    _expect_edevice("block-table page id", L.sx_full_attn, cd, lay.struct, qf, pool.struct(), of, None,
+                    wsf)
+    qd = torch.randn((1, D.n_q_heads, D.head_dim), device=DEV).to(torch.bfloat16)
+    od = torch.full((1, D.n_q_heads * D.head_dim), 5.0, dtype=torch.bfloat16, device=DEV)
+    wsd = LY.workspace(L.SX_OP_DECODE, cd, T, 0, 1, DEV)
+    _expect_edevice("block-table page id", L.sx_decode_attn, cd, lay.struct, qd, pool.struct(), od, None,
+                    wsd)
+    _expect_edevice("block-table page id", L.sx_decode_attn_noalloc, cd, lay.struct, qd, pool.struct(),
+                    od, None)
+    torch.cuda.synchronize()
+    assert bool((o == 5.0).all()) and bool((of == 5.0).all()) and bool((od == 5.0).all())
+
+
+def test_debug_reports_bad_rows_and_positions(monkeypatch):
+    monkeypatch.setenv("SX_DEBUG", "1")
+    pool, bt, lay, _ = _setup()
+    cd = LY.make_dims(D)
+    say("[debug] rows out of order")
+    rows, rs, q, o = _attn_inputs(np.array([40, 5, 63], np.int32))
+    ws = LY.workspace(L.SX_OP_SPARSE_ATTN, cd, T, 3, 1, DEV)
+    _expect_edevice("row list", L.sx_sparse_attn, cd, lay.struct, q, rows, rs, 3, pool.struct(), o, None,
+                    ws)
+    say("[debug] a row past the batch")
+    x = torch.randn((T, D.hidden), device=DEV).to(torch.bfloat16)
+    w = torch.randn((D.qkv_rows, D.hidden), device=DEV).to(torch.bfloat16)
+    bad_rows = torch.tensor([3, T + 2], dtype=torch.int32, device=DEV)
+    before = pool.k.clone()
+    _expect_edevice("row list", L.sx_recompute_kv, cd, lay.struct, x, bad_rows, 2, w, pool.struct(), None)
+    say("[debug] RoPE positions past the table")
+    far = LY.DeviceLayout(np.array([0, T], np.int32), bt, lay.rope_tab, DEV,
+                          pos_offset=np.array([40], np.int32))
+    ok_rows = torch.tensor([3, 50], dtype=torch.int32, device=DEV)
+    _expect_edevice("RoPE position", L.sx_recompute_kv, cd, far.struct, x, ok_rows, 2, w, pool.struct(),
+                    None)
+    torch.cuda.synchronize()
+    assert torch.equal(pool.k.view(torch.int16), before.view(torch.int16))
+    assert bool((o == 5.0).all())
