@@ -559,3 +559,38 @@ def test_sparse_attention_many_chunks_and_nan_tail(shape):
         ref, lref = oracle.causal_attention(q[sl], rows[sl] - seq[r], K, V)
         assert_close_bf16(og[sl], ref.reshape(len(ref), -1), what=f"O req {r}")
         assert np.max(np.abs(lg[sl] - lref)) < 2e-3
+
+
+def test_sparse_attention_split_tiles_large_values():
+    """Values far beyond fp16's range through split tiles.  Few active rows
+    (about 350 of a 3,600-token request) make every tile split into key
+    chunks, whose partial outputs are merged; V is the usual random data
+    times 2^17 (exact in bf16), so |V| reaches ~5e5.  O scales exactly with
+    V, so the bound is the usual one times 2^17."""
+    dims = SHAPES["llama"]
+    lens = [3600]
+    scale = float(2 ** 17)
+    say("[attn] split tiles, |V| ~ 1e5")
+    rng, seq, pool, kh, vh, bt = _attn_inputs(dims, lens, 57)
+    pool.v.mul_(scale)
+    vh = vh * scale
+    rows = np.union1d(np.flatnonzero(rng.random(lens[0]) < 0.1), [0, lens[0] - 1]).astype(np.int32)
+    n_rows = len(rows)
+    q = _store(rng.standard_normal((n_rows, dims.n_q_heads, dims.head_dim)), dims)
+    rope = LY.rope_table(dims.theta, dims.head_dim, 16, DEV)
+    lay = LY.DeviceLayout(seq, bt, rope, DEV)
+    cd = LY.make_dims(dims)
+    o = torch.zeros((n_rows, dims.n_q_heads * dims.head_dim), dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros((n_rows, dims.n_q_heads), dtype=torch.float32, device=DEV)
+    ws = LY.workspace(L.SX_OP_SPARSE_ATTN, cd, int(seq[-1]), n_rows, 1, DEV)
+    L.sx_sparse_attn(cd, lay.struct, torch.from_numpy(q).to(torch.bfloat16).to(DEV),
+                     torch.from_numpy(rows).to(DEV), torch.tensor([0, n_rows], dtype=torch.int32, device=DEV),
+                     n_rows, pool.struct(), o, lse, ws)
+    torch.cuda.synchronize()
+    og = o.float().cpu().double().numpy()
+    K, V = _logical(kh, vh, bt[0], 0, lens[0])
+    ref, lref = oracle.causal_attention(q, rows, K, V)
+    ref = ref.reshape(n_rows, -1)
+    assert np.abs(ref).max() > 65504.0
+    assert_close_bf16(og, ref, atol=1e-2 * scale, what="O, |V| ~ 1e5, split tiles")
+    assert np.max(np.abs(lse.cpu().double().numpy() - lref)) < 2e-3
