@@ -155,20 +155,32 @@ def mfma_peak_measure(shapes=((2048, 400), (4096, 200), (8192, 100)), reps: int 
 
 def cpu_baseline(dims, plan, n_sparse: int, T: int, reused: int, seed: int = 4242):
     """The float64 oracle on a bounded sample of one sparse layer of the same
-    workload, scaled to tokens/s per layer.  Sample (10-30 s of CPU work):
-    realign of 16 of the 1920-token passages, projection of 1024 active rows,
-    attention of 2048 active rows, and 128 Sparse-Q rows of the selection
-    probe (amortised over the sparse layers); each part is scaled by its
-    share of the layer's work."""
+    workload, scaled to tokens/s per layer.  Sample (about 10 s of CPU work
+    per repetition on 16 cores): realign of 16 of the 1920-token passages,
+    projection of 1024 active rows, attention of 2048 active rows, and 128
+    Sparse-Q rows of the selection probe (amortised over the sparse layers);
+    each part is timed best of 3 and scaled by its share of the layer's
+    work."""
     n_pass, n_rec, n_att, n_probe = 16, 1024, 2048, 128
     import oracle
     from segment_level_kv_amd import synth
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()
-                     if p.get("user_api") == "blas"] or [1])
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = max([p.get("num_threads", 1) for p in info] or [1])
+        if info:
+            blas = " / ".join(f"{p.get('internal_api', '?')} {p.get('version', '')}".strip() for p in info)
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
+
+    def best_of(fn, reps=3):
+        best = float("inf")
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            best = min(best, time.perf_counter() - t0)
+        return best
     rng = np.random.default_rng(seed)
     hkv, hq, d = dims.n_kv_heads, dims.n_q_heads, dims.head_dim
     sq = plan["sq_rows"].astype(np.int64)
@@ -181,40 +193,38 @@ def cpu_baseline(dims, plan, n_sparse: int, T: int, reused: int, seed: int = 424
     V = synth.to_storage(rng.standard_normal((T, hkv, d)), "bf16")
     t = {}
     # realign: n_pass passages, each moved by its own offset
-    t0 = time.perf_counter()
-    for i in range(n_pass):
-        a = 512 + 1920 * i
-        oracle.realign_segment(K[a:a + 1920], V[a:a + 1920], a, 2048 + 1920 * i, dims.theta, "bf16")
-    t["realign"] = (time.perf_counter() - t0) * (R / (1920 * n_pass))
+    def realign():
+        for i in range(n_pass):
+            a = 512 + 1920 * i
+            oracle.realign_segment(K[a:a + 1920], V[a:a + 1920], a, 2048 + 1920 * i, dims.theta, "bf16")
+    t["realign"] = best_of(realign) * (R / (1920 * n_pass))
     # recompute: n_rec rows
     x = synth.to_storage(synth._rmsnormed_gaussian(rng, n_rec, dims.hidden, dims.eps), "bf16")
     wq, wk, wv = synth._weights(rng, dims)
-    t0 = time.perf_counter()
-    oracle.project_rows(x, wq, wk, wv, S[:n_rec], dims.theta, hq, hkv, d, "bf16")
-    t["recompute"] = (time.perf_counter() - t0) * (len(A) / n_rec)
+    t["recompute"] = best_of(lambda: oracle.project_rows(x, wq, wk, wv, S[:n_rec], dims.theta, hq, hkv,
+                                                         d, "bf16")) * (len(A) / n_rec)
     # attention: n_att active rows, scaled by key count
     rows = np.sort(rng.choice(A, size=n_att, replace=False))
     q = synth.to_storage(rng.standard_normal((n_att, hq, d)), "bf16")
-    t0 = time.perf_counter()
-    oracle.causal_attention(q, rows, K, V)
-    t["attn"] = (time.perf_counter() - t0) * (np.sum(A + 1) / np.sum(rows + 1))
+    t["attn"] = best_of(lambda: oracle.causal_attention(q, rows, K, V)) * (np.sum(A + 1) / np.sum(rows + 1))
     # selection probe: n_probe Sparse-Q rows (LSE + scores), amortised
     qs = synth.to_storage(rng.standard_normal((n_probe, hq, d)), "bf16")
-    t0 = time.perf_counter()
-    _, lse = oracle.causal_attention(qs, sq[:n_probe], K, V)
-    oracle.attention_mass_scores(qs, sq[:n_probe], K, lse)
-    t["select"] = (time.perf_counter() - t0) * (len(sq) / n_probe) / n_sparse
+    def probe():
+        _, lse = oracle.causal_attention(qs, sq[:n_probe], K, V)
+        oracle.attention_mass_scores(qs, sq[:n_probe], K, lse)
+    t["select"] = best_of(probe) * (len(sq) / n_probe) / n_sparse
     sample_s = sum(t_ * f for t_, f in zip(
         (t["realign"], t["recompute"], t["attn"], t["select"]),
         (1920 * n_pass / R, n_rec / len(A), np.sum(rows + 1) / np.sum(A + 1),
          n_probe * n_sparse / len(sq))))
     layer_s = sum(t.values())
     return {"value": T / layer_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "blas_vendor": blas, "repeats": "best of 3 per part",
             "sample": (f"float64 NumPy oracle, one sparse layer of the same workload: realign of "
                        f"{n_pass} 1920-token passages (x R/{1920 * n_pass}), projection of {n_rec} "
                        f"active rows (x |A|/{n_rec}), attention of {n_att} active rows (x key-count "
                        f"share), {n_probe} Sparse-Q probe rows (x {len(sq)}/{n_probe}, amortised "
-                       f"over the sparse layers)"),
+                       f"over the sparse layers); each part timed best of 3"),
             "sample_cpu_seconds": round(float(sample_s), 2),
             "seconds_per_layer": layer_s, "parts_s": {k_: round(float(v), 4) for k_, v in t.items()}}
 
