@@ -440,15 +440,19 @@ sx_status sx_decode_attn_noalloc(const sx_dims *dims, const sx_layout *lay, cons
  * MFMA units, the measured counterpart of the data-sheet bf16 peak that the
  * attention utilisation is also quoted against.  Launches n_workgroups
  * workgroups of 8 waves (two per SIMD when one workgroup runs per compute
- * unit); every wave issues iters x 16 back-to-back
- * v_mfma_f32_32x32x16_bf16 (32768 flop each) on four independent
- * accumulators, so the launch performs
- *   n_workgroups * 8 * iters * 16 * 32768 flop.
- * Time it with events on `stream`.  out: device, n_workgroups * 8 floats
- * (one reduced value per wave, written so the work is not optimised away;
- * the values carry no meaning).  Errors: SX_EINVAL for n_workgroups or
- * iters outside [1, 2^20] or a NULL out; SX_EDEVICE if the launch fails. */
-sx_status sx_mfma_peak_probe(int32_t n_workgroups, int32_t iters, float *out, void *stream);
+ * unit); every wave issues iters x 16 back-to-back v_mfma_f32_32x32x16_bf16
+ * (32768 flop each), eight in a row on each of two accumulators, so the
+ * launch performs n_workgroups * 8 * iters * 16 * 32768 flop.  Operands are
+ * small constants (random_operands == 0) or random bf16 values in [-2, 2)
+ * from eight register sets in turn (random_operands != 0): the chip draws
+ * more power and holds a lower clock on random data, so the two rates
+ * bracket what an MFMA-bound kernel can reach.  Time it with events on
+ * `stream`.  out: device, n_workgroups * 8 floats (one reduced value per
+ * wave, written so the work is not optimised away; the values carry no
+ * meaning).  Errors: SX_EINVAL for n_workgroups or iters outside [1, 2^20]
+ * or a NULL out; SX_EDEVICE if the launch fails. */
+sx_status sx_mfma_peak_probe(int32_t n_workgroups, int32_t iters, int32_t random_operands, float *out,
+                             void *stream);
 
 /* Text of the last non-OK status returned on the calling thread. */
 const char *sx_last_error(void);

@@ -88,7 +88,7 @@ def lib():
             "sx_full_attn": (I, [P, P, P, P, P, P, P, Z, P]),
             "sx_decode_attn": (I, [P, P, P, P, P, P, P, Z, P]),
             "sx_decode_attn_noalloc": (I, [P, P, P, P, P, P, P]),
-            "sx_mfma_peak_probe": (I, [I, I, P, P]),
+            "sx_mfma_peak_probe": (I, [I, I, I, P, P]),
             "sx_last_error": (C.c_char_p, []),
             "sx_virtual_hash": (I, [P, I, U, P]),
             "sx_index_create": (I, [I, I, I, I, P]),
@@ -355,8 +355,9 @@ def sx_decode_attn_noalloc(dims: Dims, lay: Layout, q, kv: Pages, o, lse, stream
                                         _ptr(lse), _stream(stream)), "sx_decode_attn_noalloc")
 
 
-def sx_mfma_peak_probe(n_workgroups: int, iters: int, out, stream=None):
-    _check(lib().sx_mfma_peak_probe(int(n_workgroups), int(iters), _ptr(out), _stream(stream)),
+def sx_mfma_peak_probe(n_workgroups: int, iters: int, out, stream=None, random_operands: bool = False):
+    _check(lib().sx_mfma_peak_probe(int(n_workgroups), int(iters), 1 if random_operands else 0,
+                                    _ptr(out), _stream(stream)),
            "sx_mfma_peak_probe")
 
 

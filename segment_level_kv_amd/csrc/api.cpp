@@ -431,12 +431,13 @@ sx_status sx_decode_attn_noalloc(const sx_dims* dims, const sx_layout* lay, cons
   return launch_decode(*dims, *lay, q, *kv, o, lse, ws, as_stream(stream));
 }
 
-sx_status sx_mfma_peak_probe(int32_t n_workgroups, int32_t iters, float* out, void* stream) {
+sx_status sx_mfma_peak_probe(int32_t n_workgroups, int32_t iters, int32_t random_operands, float* out,
+                             void* stream) {
   const char* fn = "sx_mfma_peak_probe";
   SX_REQUIRE(n_workgroups >= 1 && n_workgroups <= (1 << 20), SX_EINVAL, "%s: n_workgroups must be in [1, 2^20]", fn);
   SX_REQUIRE(iters >= 1 && iters <= (1 << 20), SX_EINVAL, "%s: iters must be in [1, 2^20]", fn);
   SX_REQUIRE(out, SX_EINVAL, "%s: out is NULL", fn);
-  return launch_mfma_peak(n_workgroups, iters, out, as_stream(stream));
+  return launch_mfma_peak(n_workgroups, iters, random_operands ? 1 : 0, out, as_stream(stream));
 }
 
 sx_status sx_topk(const float* scores, const uint8_t* tok_class, const int32_t* seq_start,

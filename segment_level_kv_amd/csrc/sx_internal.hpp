@@ -105,6 +105,6 @@ class DebugCheck {
 };
 
 // Back-to-back bf16 MFMAs on every compute unit (measured-peak probe).
-sx_status launch_mfma_peak(int n_workgroups, int iters, float* out, hipStream_t stream);
+sx_status launch_mfma_peak(int n_workgroups, int iters, int random_operands, float* out, hipStream_t stream);
 
 }  // namespace sx

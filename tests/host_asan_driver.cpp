@@ -53,7 +53,7 @@ sx_status launch_scores(const sx_dims&, const sx_layout&, const void*, const int
                         hipStream_t) { reached("launch_scores"); }
 sx_status launch_topk(const float*, int, const uint8_t*, const int32_t*, int, int, const int32_t*,
                       const int32_t*, int32_t*, int32_t*, float*, void*, hipStream_t) { reached("launch_topk"); }
-sx_status launch_mfma_peak(int, int, float*, hipStream_t) { reached("launch_mfma_peak"); }
+sx_status launch_mfma_peak(int, int, int, float*, hipStream_t) { reached("launch_mfma_peak"); }
 }  // namespace sx
 
 // ---- checks ---------------------------------------------------------------
@@ -256,7 +256,7 @@ static void device_entry_validation() {
   CHECK(sx_select_topk(&d, &lay, fake_f, nullptr, fake_i, fake_i, 4, nullptr, &pages, nullptr, fake_i,
                        fake_i, nullptr, nullptr, ws, sizeof ws, nullptr) == SX_EINVAL);
   CHECK(sx_topk(nullptr, nullptr, fake_i, 1, 4, fake_i, fake_i, nullptr, 0, nullptr) == SX_EINVAL);
-  CHECK(sx_mfma_peak_probe(0, 1, fake_f, nullptr) == SX_EINVAL);
+  CHECK(sx_mfma_peak_probe(0, 1, 0, fake_f, nullptr) == SX_EINVAL);
   CHECK(std::strlen(sx_last_error()) > 0);
 }
 

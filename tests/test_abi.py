@@ -90,9 +90,9 @@ def test_validation_errors_launch_nothing():
     assert lib.sx_sparse_attn_run(C.byref(d), C.byref(lay), FAKE, FAKE, -1, C.byref(pages), FAKE, None,
                                   FAKE, 1 << 20, None) == L.SX_EINVAL
     # MFMA probe: sizes and output are checked before any launch
-    assert lib.sx_mfma_peak_probe(0, 10, FAKE, None) == L.SX_EINVAL
-    assert lib.sx_mfma_peak_probe(4, 0, FAKE, None) == L.SX_EINVAL
-    assert lib.sx_mfma_peak_probe(4, 10, None, None) == L.SX_EINVAL
+    assert lib.sx_mfma_peak_probe(0, 10, 0, FAKE, None) == L.SX_EINVAL
+    assert lib.sx_mfma_peak_probe(4, 0, 1, FAKE, None) == L.SX_EINVAL
+    assert lib.sx_mfma_peak_probe(4, 10, 0, None, None) == L.SX_EINVAL
     assert "sx_mfma_peak_probe" in L.last_error()
     # a layout with tokens but no block-table columns
     empty_bt = L.Layout(1, 16, 0, 16, 0x1000, 0x1000, None, 0x1000)

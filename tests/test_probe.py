@@ -1,6 +1,7 @@
-"""The MFMA throughput probe behind the measured-peak figure of bench.py:
-it runs through the C ABI, every wave produces the same finite value (all
-waves compute the same products), and a launch is timed."""
+"""The MFMA throughput probe behind the measured-peak figures of bench.py:
+it runs through the C ABI; with constant operands every wave produces the
+same finite value (all waves compute the same products), with random
+operands every wave produces a finite value of its own."""
 
 import numpy as np
 import pytest
@@ -21,3 +22,13 @@ def test_mfma_peak_probe_runs_and_is_uniform():
     v = out.cpu().numpy()
     assert np.all(np.isfinite(v))
     assert np.all(v == v[0])
+
+
+def test_mfma_peak_probe_random_operands_runs():
+    """Random operands: every wave writes a finite value (the values differ)."""
+    n_wg, iters = 256, 20
+    out = torch.full((n_wg * 8,), float("nan"), dtype=torch.float32, device="cuda")
+    L.sx_mfma_peak_probe(n_wg, iters, out, random_operands=True)
+    torch.cuda.synchronize()
+    v = out.cpu().numpy()
+    assert np.all(np.isfinite(v)) and len(np.unique(v)) > 1
