@@ -5,9 +5,9 @@
 //   [q | k | v] = x[rows] . W_qkv^T ;  q, k rotated by R_pos ;
 //   k, v scattered into the request's pages, q written densely.
 //
-// bf16 path: MFMA GEMM (v_mfma_f32_32x32x16_bf16), 256x128 or 256x256
-// output tiles (one or two whole heads of 128, so both halves of every
-// rotate-half pair are in the tile).  Tiles are assigned XCD-contiguously (workgroup b
+// bf16 path: MFMA GEMM (v_mfma_f32_32x32x16_bf16), 256x128, 256x256 or
+// 256x384 output tiles (one, two or three whole heads of 128, so both halves
+// of every rotate-half pair are in the tile).  Tiles are assigned XCD-contiguously (workgroup b
 // runs on XCD b % 8) and grouped 4 row-tiles at a time so that concurrently
 // running workgroups share W and X slices in their XCD's L2.  The epilogue
 // stages the fp32 tile in LDS, applies RoPE with the fp64-built table,
@@ -39,14 +39,20 @@ constexpr int NCA = BM2 * BK * 2 / 1024 / GW;   // 1 KB stage copies per wave: A
 // HPT heads (128 columns each) per tile.  HPT = 1: 48 KB stages in a ring
 // of 3, waves 4 x 2 of 64 x 64.  HPT = 2 (256 x 256 tiles, 1.5x the flops
 // per staged byte): 64 KB stages in a ring of 2, waves 2 x 4 of 128 x 64.
+// HPT = 3 (256 x 384 tiles, 1.8x): 80 KB stages in a ring of 2 (the whole
+// LDS), waves 4 x 2 of 64 x 192 (192 accumulator registers per lane, so the
+// next k-slice's operands are not read ahead).
 template <int HPT>
 struct GemmCfg {
   static constexpr int BNT = BN * HPT;              // output columns per tile
   static constexpr int NST = HPT == 1 ? 3 : 2;      // ring stages
-  static constexpr int WGN = 2 * HPT;               // waves along N (64 columns each)
+  static constexpr int WGN = HPT == 2 ? 4 : 2;      // waves along N
   static constexpr int WGM = GW / WGN;              // waves along M
   static constexpr int WROWS = BM2 / WGM;           // output rows per wave
+  static constexpr int WCOLS = BNT / WGN;           // output columns per wave
   static constexpr int MI = WROWS / 32;             // 32 x 32 MFMA tiles per wave along M
+  static constexpr int NJ = WCOLS / 32;             // ... and along N
+  static constexpr int NBUF = HPT == 3 ? 1 : 2;     // k-slices of operands in registers
   static constexpr int NCB = BNT * BK * 2 / 1024 / GW;   // 1 KB stage copies per wave: B
 };
 template <int HPT>
@@ -54,19 +60,23 @@ struct Gemm2Stage {
   uint16_t a[BM2][BK];
   uint16_t b[BN * HPT][BK];
 };
-template <int HPT>
-struct Gemm2Smem {
-  union {
-    Gemm2Stage<HPT> st[GemmCfg<HPT>::NST];
-    float c[BM2][LDC];                 // one head of the output tile at a time
-  };
-  // per output row, resolved once per tile: page of the token (-1 if the row
-  // or its page is invalid; for Q heads only row_ok matters), its slot and
-  // its RoPE position
+// The epilogue's view of the LDS, once the ring is no longer needed: one
+// head of the output tile in fp32, and per output row the page of its token
+// (-1 if the row or its page is invalid; for Q heads only row_ok matters),
+// its slot and its RoPE position.
+struct GemmEpi {
+  float c[BM2][LDC];
   int32_t row_page[BM2];
   int32_t row_slot[BM2];
   int32_t row_pos[BM2];
   int32_t row_ok[BM2];
+};
+template <int HPT>
+struct Gemm2Smem {
+  union {
+    Gemm2Stage<HPT> st[GemmCfg<HPT>::NST];
+    GemmEpi epi;
+  };
 };
 
 template <int HPT>
@@ -96,19 +106,6 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
   const int m0 = mt * BM2;
   const int head1 = head0 + HPT * nt;         // first head: 0..hq-1 Q, then K heads, then V heads
   const uint16_t* wt = w + (size_t)head1 * 128 * hidden;
-
-  if (tid < BM2) {
-    int r = -1, idx = 0;
-    if (m0 + tid < n_rows) {
-      const int tok = rows[m0 + tid];
-      r = find_request(lay.seq_start, lay.n_req, tok);
-      if (r >= 0) idx = tok - lay.seq_start[r];
-    }
-    sm.row_ok[tid] = r >= 0;
-    sm.row_page[tid] = r >= 0 ? page_of(lay, n_pages, r, idx) : -1;
-    sm.row_slot[tid] = idx & (kPage - 1);
-    sm.row_pos[tid] = r >= 0 ? rope_pos(lay, r, idx) : 0;
-  }
 
   // ---- copy plan: lane L of copy i moves one 16-byte chunk --------------
   // A: rows 8*NCA*wave + 8*i + L/8 (i < NCA); B: rows 8*NCB*wave + 8*i + L/8
@@ -153,11 +150,12 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
       __builtin_amdgcn_global_load_lds((gptr_t)(wb + b_off[i] + kb), (lptr_t)(bs + i * 1024), 16, 0, 0);
   };
 
-  f32x16 acc[MI][2];
+  constexpr int NJ = Cfg::NJ, NBUF = Cfg::NBUF;
+  f32x16 acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
 
   const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
@@ -169,8 +167,9 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NST2 - 2) * (NCA + NCB)) : "memory");
     issue(kt + NST2 - 1, (kt + NST2 - 1) % NST2);
     const Gemm2Stage<HPT>& S = sm.st[slot];
-    // Operands of k-slice ks+1 are read while the MFMAs of slice ks run.
-    bf16x8 af[2][MI], bfr[2][2];
+    // With two operand buffers the operands of k-slice ks+1 are read while
+    // the MFMAs of slice ks run.
+    bf16x8 af[NBUF][MI], bfr[NBUF][NJ];
     auto load = [&](int ks, int buf) __attribute__((always_inline)) {
       const int ch = 2 * ks + lh;              // 16-byte chunk of this lane's k range
 #pragma unroll
@@ -179,40 +178,76 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
         af[buf][i] = *reinterpret_cast<const bf16x8*>(&S.a[R][(ch ^ (R & 7)) * 8]);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int R = wn * 64 + j * 32 + lr;
+      for (int j = 0; j < NJ; ++j) {
+        const int R = wn * Cfg::WCOLS + j * 32 + lr;
         bfr[buf][j] = *reinterpret_cast<const bf16x8*>(&S.b[R][(ch ^ (R & 7)) * 8]);
       }
     };
-    load(0, 0);
+    if (NBUF == 2) {
+      load(0, 0);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) load(ks + 1, (ks + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);     // keep those reads ahead of this slice's MFMAs
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        if (ks + 1 < BK / 16) load(ks + 1, (ks + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of this slice's MFMAs
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
+      }
+    } else {
+      // one operand buffer: the A fragments of a slice, then each B fragment
+      // just before its MFMAs (few operand registers live next to 192
+      // accumulators)
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int ch = 2 * ks + lh;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const int R = wm * WROWS + i * 32 + lr;
+          af[0][i] = *reinterpret_cast<const bf16x8*>(&S.a[R][(ch ^ (R & 7)) * 8]);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int R = wn * Cfg::WCOLS + j * 32 + lr;
+          const bf16x8 bj = *reinterpret_cast<const bf16x8*>(&S.b[R][(ch ^ (R & 7)) * 8]);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bj, acc[i][j], 0, 0, 0);
+        }
+      }
     }
   }
   // all copies landed and every wave done with the ring before it becomes C
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  GemmEpi& ep = sm.epi;
+  if (tid < BM2) {
+    int r = -1, idx = 0;
+    if (m0 + tid < n_rows) {
+      const int tok = rows[m0 + tid];
+      r = find_request(lay.seq_start, lay.n_req, tok);
+      if (r >= 0) idx = tok - lay.seq_start[r];
+    }
+    ep.row_ok[tid] = r >= 0;
+    ep.row_page[tid] = r >= 0 ? page_of(lay, n_pages, r, idx) : -1;
+    ep.row_slot[tid] = idx & (kPage - 1);
+    ep.row_pos[tid] = r >= 0 ? rope_pos(lay, r, idx) : 0;
+  }
 
   // ---- epilogue, one head at a time: its fp32 columns -> LDS -------------
   for (int h = 0; h < HPT; ++h) {
   if (h > 0) __syncthreads();                  // every thread done with the previous head
-  if (wn / 2 == h) {
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int col = wn * Cfg::WCOLS + j * 32;  // first tile column of this 32-column block
+    if (col / BN != h) continue;               // wave-uniform
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm * WROWS + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const int c = (wn & 1) * 64 + j * 32 + (lane & 31);
-          sm.c[r][c] = acc[i][j][v];
-        }
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * WROWS + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        ep.c[r][col % BN + (lane & 31)] = acc[i][j][v];
+      }
   }
   __syncthreads();
   const int head = head1 + h;
@@ -229,7 +264,7 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
 #pragma unroll
     for (int k = 0; k < kUnits; ++k) {
       const int m = (tid >> 3) + (GT / 8) * k;
-      const f32x4* tab = reinterpret_cast<const f32x4*>(lay.rope_tab + (size_t)sm.row_pos[m] * 128 + c * 16);
+      const f32x4* tab = reinterpret_cast<const f32x4*>(lay.rope_tab + (size_t)ep.row_pos[m] * 128 + c * 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) tabv[k][i] = tab[i];
     }
@@ -238,15 +273,15 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
       const int m = (tid >> 3) + (GT / 8) * k;
       uint16_t* dst = nullptr;
       if (is_q) {
-        if (q_out && sm.row_ok[m]) dst = q_out + ((size_t)(m0 + m) * hq + head) * 128;
+        if (q_out && ep.row_ok[m]) dst = q_out + ((size_t)(m0 + m) * hq + head) * 128;
       } else {
-        const int page = sm.row_page[m];
-        if (page >= 0) dst = kpool + (((size_t)page * hkv + g) * kPage + sm.row_slot[m]) * 128;
+        const int page = ep.row_page[m];
+        if (page >= 0) dst = kpool + (((size_t)page * hkv + g) * kPage + ep.row_slot[m]) * 128;
       }
       float olo[8], ohi[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float lo = sm.c[m][c * 8 + e], hi = sm.c[m][64 + c * 8 + e];
+        const float lo = ep.c[m][c * 8 + e], hi = ep.c[m][64 + c * 8 + e];
         const float cs = tabv[k][e >> 1][2 * (e & 1)], sn = tabv[k][e >> 1][2 * (e & 1) + 1];
         olo[e] = lo * cs - hi * sn;
         ohi[e] = lo * sn + hi * cs;
@@ -268,12 +303,12 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
     const int g = head - hq - hkv;
     constexpr int kDim = 128 * BM2 / GT;     // head dimensions per thread
     const int row = tid % BM2, e0 = (tid / BM2) * kDim;
-    const int page = sm.row_page[row];
+    const int page = ep.row_page[row];
     if (page >= 0) {
-      uint16_t* base = vpool + ((size_t)page * hkv + g) * 128 * kPage + sm.row_slot[row];
+      uint16_t* base = vpool + ((size_t)page * hkv + g) * 128 * kPage + ep.row_slot[row];
 #pragma unroll 4
       for (int e = e0; e < e0 + kDim; e += 4) {
-        const f32x4 c4 = *reinterpret_cast<const f32x4*>(&sm.c[row][e]);
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(&ep.c[row][e]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) base[(e + i) * kPage] = f2bf(c4[i]);
       }
@@ -451,19 +486,29 @@ __global__ __launch_bounds__(128) void qkv_rows_f32(
   }
 }
 
-// Two heads per tile or one: one workgroup fills a compute unit (256 of
-// them), so the launch takes about ceil(tiles / 256) rounds, and a two-head
-// tile takes about 1.8x a one-head tile (measured: 1.45 against 1.61 ms for
-// 31,488 rows, i.e. 2 x 0.90).  Two heads when that round count is lower,
-// e.g. for a full layer's QKV; one for a few thousand rows, where two-head
-// tiles would leave the last round mostly idle (3,379 rows: 0.251 against
-// 0.216 ms).
+// Heads per tile: one workgroup fills a compute unit (256 of them), so a
+// launch takes about ceil(tiles / 256) rounds, and a round of two-head tiles
+// costs about 1.7 rounds of one-head tiles, one of three-head tiles about
+// 2.6 (measured at 870 to 31,488 rows: the per-tile time grows less than
+// the work because fewer bytes are staged per flop).  The launcher takes the
+// cheapest, e.g. three heads for 3,379 rows (224 tiles, one round: 0.228
+// against 0.240 ms with one head), two for 13,824 or 31,488 rows, one for a
+// few hundred.
 constexpr int kGemmCUs = 256;
-bool gemm_two_heads(int mt, int n_heads) {
-  if (n_heads % 2 != 0) return false;
-  const long long t1 = (long long)mt * n_heads, t2 = t1 / 2;
-  const long long r1 = (t1 + kGemmCUs - 1) / kGemmCUs, r2 = (t2 + kGemmCUs - 1) / kGemmCUs;
-  return 9 * r2 < 5 * r1;
+int gemm_heads_per_tile(int mt, int n_heads) {
+  static const int cost10[4] = {0, 10, 17, 26};
+  int best = 1;
+  long long best_cost = -1;
+  for (int hpt = 1; hpt <= 3; ++hpt) {
+    if (n_heads % hpt != 0) continue;
+    const long long tiles = (long long)mt * (n_heads / hpt);
+    const long long cost = (tiles + kGemmCUs - 1) / kGemmCUs * cost10[hpt];
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = hpt;
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -498,9 +543,10 @@ sx_status launch_recompute(const sx_dims& dims, const sx_layout& lay, const void
           lay, kv.n_pages, (uint16_t*)kv.k, (uint16_t*)kv.v, (uint16_t*)q_out, hq, hkv);
       return SX_OK;
     };
-    const sx_status st = gemm_two_heads(mt, n_heads)
-                             ? go(qkv_gemm256_bf16<2>, 2, sizeof(Gemm2Smem<2>))
-                             : go(qkv_gemm256_bf16<1>, 1, sizeof(Gemm2Smem<1>));
+    const int hpt = gemm_heads_per_tile(mt, n_heads);
+    const sx_status st = hpt == 3   ? go(qkv_gemm256_bf16<3>, 3, sizeof(Gemm2Smem<3>))
+                         : hpt == 2 ? go(qkv_gemm256_bf16<2>, 2, sizeof(Gemm2Smem<2>))
+                                    : go(qkv_gemm256_bf16<1>, 1, sizeof(Gemm2Smem<1>));
     if (st != SX_OK) return st;
   } else {
     dim3 grid(n_rows, n_heads);

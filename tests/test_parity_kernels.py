@@ -182,15 +182,17 @@ def test_recompute_parity_and_scatter(shape, n_rows):
                 assert np.array_equal(after_v[p, :, :, sl], before_v[p, :, :, sl])
 
 
-def test_recompute_two_heads_per_tile_sampled():
-    """Row counts whose launch takes 256 x 256 tiles (two heads per tile):
-    5,200 of 6,000 tokens in Llama shapes, once with Q (48 heads) and once
-    K/V only (16 heads).  The oracle projects 320 sampled rows, spread over
-    every row tile and including the last, partial one; both heads of every
-    tile are compared, and exactly the listed rows' slots are written."""
+@pytest.mark.parametrize("n_rows", [5200, 3379])
+def test_recompute_multi_head_tiles_sampled(n_rows):
+    """Row counts whose launch takes multi-head tiles: 5,200 of 6,000 tokens
+    in Llama shapes take 256 x 256 tiles (two heads), with Q (48 heads) and
+    K/V only (16 heads); 3,379 rows (the rag32k active-set size) take
+    256 x 384 tiles (three heads) with Q, one-head tiles K/V only.  The
+    oracle projects 320 sampled rows, spread over every row tile and
+    including the last, partial one; every head of every tile is compared,
+    and exactly the listed rows' slots are written."""
     dims = SHAPES["llama"]
-    n_rows = 5200
-    say(f"[recompute] two heads per tile: rows={n_rows}")
+    say(f"[recompute] multi-head tiles: rows={n_rows}")
     rng = np.random.default_rng(23)
     seq = np.array([0, 4000, 6000], np.int32)
     n_tok = int(seq[-1])
