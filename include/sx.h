@@ -357,7 +357,9 @@ sx_status sx_select_topk(const sx_dims *dims, const sx_layout *lay, const void *
  * k_sel[r] tokens with tok_class 0 and the largest scores[j] (-0.0 equals
  * +0.0; ties: lower id first), ascending, at offset sum_{r'<r} k_sel[r'].
  * NaN scores give an unspecified (but in-bounds) selection.
- * ws: sx_workspace_bytes(SX_OP_TOPK, ...) bytes. */
+ * ws: sx_workspace_bytes(SX_OP_TOPK, dims, n_tok, 0, n_req) bytes (per-request
+ * digit histograms and per-chunk counts of the multi-workgroup radix select);
+ * a smaller or NULL ws returns SX_EWORKSPACE. */
 sx_status sx_topk(const float *scores, const uint8_t *tok_class, const int32_t *seq_start,
                   int32_t n_req, int32_t n_tok, const int32_t *k_sel, int32_t *sel_rows,
                   void *ws, size_t ws_bytes, void *stream);

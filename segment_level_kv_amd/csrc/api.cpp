@@ -444,10 +444,12 @@ sx_status sx_topk(const float* scores, const uint8_t* tok_class, const int32_t* 
                   int32_t n_req, int32_t n_tok, const int32_t* k_sel, int32_t* sel_rows, void* ws,
                   size_t ws_bytes, void* stream) {
   const char* fn = "sx_topk";
-  (void)ws_bytes;
   SX_REQUIRE(n_req >= 1 && n_req <= kMaxReq, SX_EINVAL, "%s: n_req must be in [1, %d]", fn, kMaxReq);
   SX_REQUIRE(n_tok >= 0, SX_EINVAL, "%s: n_tok < 0", fn);
   SX_REQUIRE(scores && tok_class && seq_start && k_sel && sel_rows, SX_EINVAL, "%s: NULL argument", fn);
+  const size_t need = topk_ws_bytes(n_tok, n_req);
+  SX_REQUIRE(ws && ws_bytes >= need, SX_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn,
+             need, ws ? ws_bytes : (size_t)0);
   return launch_topk(scores, 1, tok_class, seq_start, n_req, n_tok, k_sel, nullptr, sel_rows, nullptr,
                      const_cast<float*>(scores), ws, as_stream(stream));
 }
@@ -495,11 +497,14 @@ sx_status sx_select_topk(const sx_dims* dims, const sx_layout* lay, const void* 
   }
   if (lay->n_tok > 0) {
     // with no Sparse-Q rows the score kernels write zeros (no query is read)
+    // the gathered Sparse-Q rows reuse the probe's work-list space (the probe is done)
     SX_TRY(launch_scores(*dims, *lay, q, q_index, sq_rows, sq_start, n_sq, lse_use, lse_index, *kv,
-                         partial, s));
+                         partial, attn_ws, s));
   }
-  return launch_topk(partial, score_parts(*dims, lay->n_tok, lay->n_req), tok_class, lay->seq_start, lay->n_req, lay->n_tok,
-                     k_sel, sq_start, sel_rows, act_rows, scores ? scores : score_buf, nullptr, s);
+  // the top-k records reuse the same space (the score pass is done)
+  return launch_topk(partial, score_parts(*dims, lay->n_tok, lay->n_req), tok_class, lay->seq_start,
+                     lay->n_req, lay->n_tok, k_sel, sq_start, sel_rows, act_rows,
+                     scores ? scores : score_buf, attn_ws, s);
 }
 
 }  // extern "C"

@@ -8,21 +8,27 @@
 // Score pass (bf16): one workgroup per (256-key tile of a request, kv head)
 // taking the G query heads of the group in turn, or, when that grid would
 // leave compute units idle (short prompts), per (tile, query head); each
-// wave keeps the K operand of its 64 keys in registers, the Sparse-Q rows of
-// one query head stream through LDS 32 at a time, S = Q . K^T runs on
+// wave keeps the K operand of its 64 keys in registers, the Sparse-Q rows
+// stream through LDS two 32-row blocks per stage, S = Q . K^T runs on
 // v_mfma_f32_32x32x16_bf16 with the key axis across lanes, and each lane
-// sums exp(S - lse) over the queries in registers.  Partial sums per
-// workgroup row go to a [parts][n_tok] buffer (parts = Hkv or Hq); the top-k
-// kernel adds them in row order, so every score is the same fixed-order fp32
-// sum run to run.
+// sums exp(S - lse) over the queries in registers.  The MFMAs of the next
+// block are issued before the exponentials of the current one, so the
+// matrix cores and the VALU overlap inside each wave; the causal mask is
+// applied only in blocks whose first row precedes the wave's last key.
+// Partial sums per workgroup row go to a [parts][n_tok] buffer
+// (parts = Hkv or Hq); the top-k adds them in row order, so every score is
+// the same fixed-order fp32 sum run to run.
 //
-// Top-k: one workgroup per request.  Order-preserving 32-bit keys of the
-// scores (-0 mapped to +0), a 4-pass 8-bit radix select for the k-th largest
-// key in LDS (per-wave histograms), then an in-order compaction sweep with
-// block prefix sums: all keys above the threshold plus the lowest-indexed
-// keys equal to it.  Output is ascending by token id.  Every sweep issues a
-// batch of loads per thread before using them (one workgroup per request
-// would otherwise pay a memory round trip per element).
+// Top-k: a multi-workgroup radix select over order-preserving 32-bit keys
+// of the scores (-0 mapped to +0) with three digits and per-request global
+// histograms, then per-chunk counts and an ordered compaction: all keys
+// above the k-th largest plus the lowest-indexed keys equal to it, output
+// ascending by token id.  Integer atomics only, so the result does not
+// depend on the order workgroups run in.
+#include <algorithm>
+#include <climits>
+#include <type_traits>
+
 #include "sx_device.hpp"
 #include "sx_internal.hpp"
 
@@ -30,13 +36,18 @@ namespace sx {
 
 namespace {
 
-constexpr int SKT = 256;        // keys per score workgroup
-constexpr int SQB = 32;         // Sparse-Q rows per LDS block
+constexpr int SKT = 256;        // keys per score workgroup (4 waves x 64)
+constexpr int SQB = 32;         // Sparse-Q rows per block (one MFMA row tile)
+constexpr int SBS = 2;          // blocks per LDS stage
+constexpr int SQP = 128 + 8;    // LDS row pitch in bf16 elements (16-byte pad: conflict-free b128 reads)
 
+// Q rows are read when a block's MFMAs are issued, the normalisers and
+// positions one block later (with its exponentials), hence three buffers
+// for those.
 struct ScoreSmem {
-  uint16_t q[SQB][128 + 8];
-  float lse2[SQB];
-  int32_t qpos[SQB];
+  uint16_t q[2][SBS * SQB][SQP];   // two stages of SBS blocks
+  float lse2[3][SBS * SQB];        // log2-domain normaliser of each row (+inf: no row)
+  int32_t qpos[3][SBS * SQB];      // row position in its request (INT_MAX: no row)
 };
 
 // Tile t of the score grid -> (request, first key index).  Tiles are laid
@@ -56,12 +67,52 @@ __device__ __forceinline__ bool score_tile(const int32_t* seq_start, int n_req, 
   return false;
 }
 
-__global__ __launch_bounds__(256) void scores_bf16(
+// One Sparse-Q block in flight: S = Q_blk . K^T for the wave's two 32-key
+// columns.
+struct ScoreBlock {
+  f32x16 s[2];
+};
+
+// Sparse-Q row i of the batch into the score pass's layout: its q rows
+// (q[q_index[i]], all heads) copied to q_g[i], its normalisers
+// lse[lse_index[i]] times log2(e) to lse2_g[h][i] (head-major, so a block's
+// 32 rows are one 128-byte line), and its position in its request to
+// pos_g[i].  One workgroup per row.
+__global__ __launch_bounds__(256) void sq_gather(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_index,
+    const float* __restrict__ lse, const int32_t* __restrict__ lse_index,
     const int32_t* __restrict__ sq_rows, const int32_t* __restrict__ sq_start,
-    const float* __restrict__ lse, const int32_t* __restrict__ lse_index, sx_layout lay,
+    const int32_t* __restrict__ seq_start, int n_req, int n_sq, int hq, uint16_t* __restrict__ q_g,
+    float* __restrict__ lse2_g, int32_t* __restrict__ pos_g) {
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int qr = q_index ? q_index[i] : i;
+  const u32x4* src = reinterpret_cast<const u32x4*>(q + (size_t)qr * hq * 128);
+  u32x4* dst = reinterpret_cast<u32x4*>(q_g + (size_t)i * hq * 128);
+  for (int c = tid; c < hq * 16; c += 256) dst[c] = src[c];
+  if (tid < hq) {
+    const int lr = lse_index ? lse_index[i] : i;
+    lse2_g[(size_t)tid * n_sq + i] = lse[(size_t)lr * hq + tid] * kLog2e;
+  }
+  if (tid == 0) {
+    // the request owning row i: the last r < n_req with sq_start[r] <= i
+    int lo = 0, hi = n_req;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sq_start[mid] <= i) lo = mid;
+      else hi = mid;
+    }
+    pos_g[i] = sq_rows[i] - seq_start[lo];
+  }
+}
+
+// Sparse-Q rows in the score pass's layout (sq_gather above): row i of the
+// batch's Sparse-Q list at q_g[i][h][:], its normalisers times log2(e) at
+// lse2_g[h][i] and its position in its request at pos_g[i].
+__global__ __launch_bounds__(256) void scores_bf16(
+    const uint16_t* __restrict__ q_g, const float* __restrict__ lse2_g,
+    const int32_t* __restrict__ pos_g, const int32_t* __restrict__ sq_start, sx_layout lay,
     int n_pages, const uint16_t* __restrict__ kpool, int hq, int hkv,
-    float* __restrict__ partial, float scale_log2, int hpw) {
+    float* __restrict__ partial, float scale_log2, int hpw, int n_sq) {
   __shared__ ScoreSmem sm;
   int req, k0;
   if (!score_tile(lay.seq_start, lay.n_req, blockIdx.x, req, k0)) return;
@@ -92,85 +143,179 @@ __global__ __launch_bounds__(256) void scores_bf16(
       kf[nb][kk] = __builtin_bit_cast(bf16x8, raw);
     }
   }
+  const int kmax_w = k0 + 64 * w + 63;        // largest key of the wave
 
+  // The Sparse-Q blocks that reach this key tile, head by head: block it is
+  // rows bfirst + 32 (it % n_blk) .. of head h0 + it / n_blk.  Sparse-Q rows
+  // are ascending, so the blocks wholly before the tile form a prefix that is
+  // skipped.  Stage st (LDS buffer st & 1) holds blocks 2st and 2st + 1.
   const int s0 = sq_start[req], s1 = sq_start[req + 1];
-  float acc[2] = {0.f, 0.f};
-  // The Sparse-Q blocks that reach this key tile, visited head by head; the
-  // next block's Q rows, LSE and positions are loaded into registers while
-  // the current block is in the MFMAs.  Sparse-Q rows are ascending, so the
-  // blocks wholly before the tile form a prefix that is skipped.
   int bfirst = s0;
-  while (bfirst < s1 && sq_rows[min(bfirst + SQB, s1) - 1] - seq0 < k0) bfirst += SQB;
+  while (bfirst < s1 && pos_g[min(bfirst + SQB, s1) - 1] < k0) bfirst += SQB;
   const int n_blk = (s1 - bfirst + SQB - 1) / SQB;
-  const int n_it = n_blk * hpw;              // iteration it: head h0 + it / n_blk, block it % n_blk
-  constexpr int QU = SQB * 16 / 256;         // 16-byte Q chunks per thread and block
+  const int n_it = n_blk * hpw;
+  const int n_st = (n_it + SBS - 1) / SBS;
+  constexpr int QU = SBS * SQB * 16 / 256;    // 16-byte Q chunks per thread and stage
+  // Loads of stage st go to registers one stage ahead of their LDS store.
+  // They are unconditional: an absent row reads row s0 of head h0, whose
+  // finite q values are harmless because the row's normaliser is stored as
+  // +inf (every exponential of the row is 0).  A load under a branch would
+  // make the wait-count analysis drain every load in flight at the join.
   u32x4 qn[QU];
-  float lse_n = INFINITY;
-  int pos_n = -1;
-  auto fetch = [&](int it) __attribute__((always_inline)) {
-    const int h = h0 + it / n_blk;
-    const int b0 = bfirst + (it % n_blk) * SQB;
+  float lse_n = 0.f;
+  int pos_n = 0;
+  bool okl = false;             // row tid (< SBS * SQB) exists
+  int ix_b = 0, ix_h = h0;      // block-in-head and head of the next stage's first block
+  const int lrow = tid & (SBS * SQB - 1);
+  auto fetch = [&](int st) __attribute__((always_inline)) {
+    int bb[SBS], hh[SBS];
+#pragma unroll
+    for (int k = 0; k < SBS; ++k) {
+      const bool real = SBS * st + k < n_it;
+      bb[k] = real ? ix_b : 0;
+      hh[k] = real ? ix_h : h0;
+      if (++ix_b == n_blk) {
+        ix_b = 0;
+        ++ix_h;
+      }
+    }
 #pragma unroll
     for (int e = 0; e < QU; ++e) {
       const int u = tid + 256 * e;
-      const int r = u >> 4, c = u & 15;
-      const int i = b0 + r;
-      qn[e] = u32x4{0, 0, 0, 0};
-      if (i < s1) {
-        const int qr = q_index ? q_index[i] : i;
-        qn[e] = *reinterpret_cast<const u32x4*>(q + ((size_t)qr * hq + h) * 128 + c * 8);
+      const int row = u >> 4, blk = row >> 5;
+      const int i = bfirst + bb[blk] * SQB + (row & 31);
+      const int ic = (SBS * st + blk < n_it && i < s1) ? i : s0;
+      qn[e] = *reinterpret_cast<const u32x4*>(q_g + ((size_t)ic * hq + hh[blk]) * 128 + (u & 15) * 8);
+    }
+    const int blk = lrow >> 5;
+    const int i = bfirst + bb[blk] * SQB + (lrow & 31);
+    okl = tid < SBS * SQB && SBS * st + blk < n_it && i < s1;
+    const int ic = okl ? i : s0;
+    lse_n = lse2_g[(size_t)hh[blk] * n_sq + ic];
+    pos_n = pos_g[ic];
+  };
+  auto stage_store = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < QU; ++e) {
+      const int u = tid + 256 * e;
+      *reinterpret_cast<u32x4*>(&sm.q[st & 1][u >> 4][(u & 15) * 8]) = qn[e];
+    }
+    if (tid < SBS * SQB) {
+      sm.lse2[st % 3][tid] = okl ? lse_n : INFINITY;
+      sm.qpos[st % 3][tid] = okl ? pos_n : INT_MAX;
+    }
+  };
+  // S of block it; its Q rows are read from LDS here.
+  auto issue = [&](int it, ScoreBlock& b) __attribute__((always_inline)) {
+    const uint16_t* qr = &sm.q[(it / SBS) & 1][(it % SBS) * SQB + (lane & 31)][hl * 8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(qr + kk * 16);
+      b.s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[0][kk], kk ? b.s[0] : f32x16{}, 0, 0, 0);
+      b.s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[1][kk], kk ? b.s[1] : f32x16{}, 0, 0, 0);
+    }
+  };
+  // Four accumulators per key column, added in a fixed order at the end.
+  float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // Causal mask (row position >= key): only a block whose first row
+  // precedes the wave's last key needs it (rows are ascending; the test is
+  // wave-uniform).
+  auto needs_mask = [&](int it) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane(sm.qpos[(it / SBS) % 3][(it % SBS) * SQB]) <
+           __builtin_amdgcn_readfirstlane(kmax_w);
+  };
+  // The exponentials of block itA (S in a) and, when ISSUE, the MFMAs of
+  // block itB (into b) interleaved in one straight-line region, so each
+  // wave keeps its matrix core and its VALU busy at the same time: two
+  // MFMAs per eight-byte step of the head dimension, four of the 32
+  // exponentials of the lane after each.
+  auto step = [&](auto mask_c, auto issue_c, int itA, const ScoreBlock& a, int itB,
+                  ScoreBlock& b) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value, ISSUE = decltype(issue_c)::value;
+    const int bufA = (itA / SBS) % 3, rbA = (itA % SBS) * SQB;
+    // accumulator register v of lane half hl holds block row 8(v>>2)+4hl+(v&3)
+    float l[16];
+    int qp[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[bufA][rbA + 8 * q4 + 4 * hl]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) l[4 * q4 + e] = l4[e];
+      if (MASK) {
+        const u32x4 p4 = *reinterpret_cast<const u32x4*>(&sm.qpos[bufA][rbA + 8 * q4 + 4 * hl]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qp[4 * q4 + e] = (int)p4[e];
       }
     }
-    if (tid < SQB) {
-      const int i = b0 + tid;
-      lse_n = INFINITY;
-      pos_n = -1;
-      if (i < s1) {
-        const int lr = lse_index ? lse_index[i] : i;
-        lse_n = lse[(size_t)lr * hq + h] * kLog2e;
-        pos_n = sq_rows[i] - seq0;
+    const uint16_t* qr = &sm.q[(itB / SBS) & 1][(itB % SBS) * SQB + (lane & 31)][hl * 8];
+    // v_exp_f32 directly: the argument is a log2 probability (<= 0 up to
+    // rounding); below 2^-126 the term is below any score tolerance.
+    auto elem = [&](int e) __attribute__((always_inline)) {
+      const int nb = e >> 4, v = e & 15;
+      float p = __builtin_amdgcn_exp2f(fmaf(a.s[nb][v], scale_log2, -l[v]));
+      if (MASK) p = qp[v] >= key_idx[nb] ? p : 0.f;
+      acc[nb][v & 3] += p;
+    };
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      if (ISSUE) {
+        const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(qr + kk * 16);
+        b.s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q8, kf[0][kk], kk ? b.s[0] : f32x16{}, 0, 0, 0);
+        elem(4 * kk);
+        elem(4 * kk + 1);
+        b.s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q8, kf[1][kk], kk ? b.s[1] : f32x16{}, 0, 0, 0);
+        elem(4 * kk + 2);
+        elem(4 * kk + 3);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) elem(4 * kk + e);
       }
     }
   };
-  if (n_it > 0) fetch(0);
-  for (int it = 0; it < n_it; ++it) {
-    {
-      __syncthreads();                        // every wave is done with the previous block
-#pragma unroll
-      for (int e = 0; e < QU; ++e) {
-        const int u = tid + 256 * e;
-        *reinterpret_cast<u32x4*>(&sm.q[u >> 4][(u & 15) * 8]) = qn[e];
-      }
-      if (tid < SQB) {
-        sm.lse2[tid] = lse_n;
-        sm.qpos[tid] = pos_n;
-      }
-      __syncthreads();
-      if (it + 1 < n_it) fetch(it + 1);
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-      const uint16_t* qr = &sm.q[lane & 31][hl * 8];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qr + kk * 16);
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[0][kk], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[1][kk], s[1], 0, 0, 0);
-      }
-      // accumulator register v of lane half hl holds query row 8(v>>2)+4hl+(v&3)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int qr_ = 8 * (v >> 2) + 4 * hl + (v & 3);
-          // v_exp_f32 directly: the argument is a log2 probability (<= 0 up to
-          // rounding); below 2^-126 the term is below any score tolerance.
-          const float p = __builtin_amdgcn_exp2f(s[nb][v] * scale_log2 - sm.lse2[qr_]);
-          acc[nb] += (sm.qpos[qr_] >= key_idx[nb]) ? p : 0.f;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  auto step_issue = [&](int itA, const ScoreBlock& a, int itB, ScoreBlock& b) __attribute__((always_inline)) {
+    if (needs_mask(itA)) step(T_{}, T_{}, itA, a, itB, b);
+    else step(F_{}, T_{}, itA, a, itB, b);
+  };
+  auto step_last = [&](int itA, const ScoreBlock& a) __attribute__((always_inline)) {
+    ScoreBlock none;
+    if (needs_mask(itA)) step(T_{}, F_{}, itA, a, itA, none);
+    else step(F_{}, F_{}, itA, a, itA, none);
+  };
+
+  if (n_it > 0) {
+    fetch(0);
+    stage_store(0);
+    __syncthreads();
+    if (n_st > 1) fetch(1);
+    ScoreBlock A, B;
+    issue(0, A);
+    // Software pipeline: block it+1's MFMAs run with block it's
+    // exponentials.  Block it+1 may lie past the last block (odd n_it): its
+    // MFMAs then read a stage buffer's stale rows and are never consumed.
+    for (int it = 0; it < n_it; it += 2) {
+      step_issue(it, A, it + 1, B);
+      if (it + 2 < n_it) {
+        if ((it + 2) % SBS == 0) {
+          // Stage st's Q buffer was last read by the MFMAs of stage st - 2
+          // and its normaliser buffer by the exponentials of stage st - 3;
+          // every wave finished both before the previous barrier.
+          const int st = (it + 2) / SBS;
+          stage_store(st);
+          __syncthreads();
+          if (st + 1 < n_st) fetch(st + 1);
         }
+        step_issue(it + 1, B, it + 2, A);
+      } else if (it + 1 < n_it) {
+        step_last(it + 1, B);
+      }
     }
   }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const float tot = acc[nb] + __shfl_xor(acc[nb], 32);
+    const float own = (acc[nb][0] + acc[nb][1]) + (acc[nb][2] + acc[nb][3]);
+    const float tot = own + __shfl_xor(own, 32);
     if (hl == 0 && key_idx[nb] < len) partial[(size_t)blockIdx.y * lay.n_tok + seq0 + key_idx[nb]] = tot;
   }
 }
@@ -215,13 +360,40 @@ __global__ __launch_bounds__(256) void scores_f32(
 // ---------------------------------------------------------------------------
 // Top-k
 // ---------------------------------------------------------------------------
+//
+// Each request's tokens are cut into chunks of TK_CHUNK; every kernel below
+// runs one workgroup per chunk.  Candidates are ordered by a 32-bit key
+// (order_key of the score); the k-th largest key is found by a radix select
+// over three digits (key bits 31-21, 20-10, 9-0): pass p counts, per
+// request, the digits of the keys that share the digits already chosen,
+// in a global histogram (integer atomics, so the counts do not depend on
+// the order the workgroups run in), and every workgroup of the next kernel
+// reads the histograms and picks the digit itself.  Then each chunk counts
+// its keys above / equal to the threshold, and the last kernel places each
+// chunk's selected tokens after those of the chunks before it (ties at the
+// threshold go to the lowest token ids), in ascending token order.
 
-constexpr int TK_THREADS = 1024;
+constexpr int TK_THREADS = 256;
 constexpr int TK_WAVES = TK_THREADS / 64;
-constexpr int TK_BATCH = 8;           // rounds of TK_THREADS tokens loaded together
+constexpr int TK_PER = 4;                        // consecutive tokens per thread
+constexpr int TK_CHUNK = TK_THREADS * TK_PER;    // tokens per workgroup
+constexpr int TK_BINS0 = 2048, TK_BINS1 = 2048, TK_BINS2 = 1024;
 
-struct TopkSmem {
-  uint32_t hist[TK_WAVES][256];
+// Per-request record in the workspace.
+struct TopkReq {
+  uint32_t hist0[TK_BINS0];    // key bits 31-21 of the candidates
+  uint32_t hist1[TK_BINS1];    // bits 20-10 of the candidates matching the chosen bits 31-21
+  uint32_t hist2[TK_BINS2];    // bits 9-0 of those matching bits 31-10
+  int32_t n_cand;
+  int32_t pad[63];
+};
+// Per-chunk counts: keys above the threshold, keys equal to it, class-1 tokens.
+struct TopkChunk {
+  int32_t gt, eq, c1, pad;
+};
+
+struct TkSmem {
+  uint32_t hist[TK_BINS0];
   int32_t wsum[TK_WAVES];
   int32_t bcast[4];
 };
@@ -232,8 +404,8 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Exclusive prefix sum over the workgroup; *total receives the sum.
-__device__ int block_scan(int v, TopkSmem& sm, int* total) {
+// Exclusive prefix sum over the workgroup in thread order; *total gets the sum.
+__device__ int tk_scan(int v, TkSmem& sm, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int x = v;
 #pragma unroll
@@ -244,6 +416,7 @@ __device__ int block_scan(int v, TopkSmem& sm, int* total) {
   if (lane == 63) sm.wsum[w] = x;
   __syncthreads();
   int before = 0, tot = 0;
+#pragma unroll
   for (int i = 0; i < TK_WAVES; ++i) {
     const int s = sm.wsum[i];
     before += (i < w) ? s : 0;
@@ -254,167 +427,334 @@ __device__ int block_scan(int v, TopkSmem& sm, int* total) {
   return before + x - v;
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_kernel(
-    const float* __restrict__ partial, int n_parts, int n_tok, const uint8_t* __restrict__ tok_class,
-    const int32_t* __restrict__ seq_start, const int32_t* __restrict__ k_sel,
-    const int32_t* __restrict__ sq_start, int32_t* __restrict__ sel_rows,
-    int32_t* __restrict__ act_rows, float* __restrict__ scores) {
-  __shared__ TopkSmem sm;
+// Chunk c of the grid -> request and the grid index of the request's first
+// chunk.  Chunks are laid out request by request, ceil(len / TK_CHUNK) each.
+__device__ __forceinline__ bool tk_chunk(const int32_t* seq_start, int n_req, int c, int& req,
+                                         int& first) {
+  int base = 0;
+  for (int r = 0; r < n_req; ++r) {
+    const int nc = (seq_start[r + 1] - seq_start[r] + TK_CHUNK - 1) / TK_CHUNK;
+    if (c < base + nc) {
+      req = r;
+      first = base;
+      return true;
+    }
+    base += nc;
+  }
+  return false;
+}
+
+// The digit holding the want-th largest key (1 <= want <= the histogram's
+// total) and the key's rank among the keys with that digit.  Thread t looks
+// at bins NB-1-PER*t down to NB-PER*(t+1), so thread order is descending
+// digit order.
+template <int NB>
+__device__ void tk_pick(const uint32_t* __restrict__ hist, int want, TkSmem& sm, uint32_t* digit,
+                        int* rem) {
+  constexpr int PER = NB / TK_THREADS;
+  const int tid = threadIdx.x;
+  int c[PER];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = (int)hist[NB - 1 - PER * tid - i];
+    s += c[i];
+  }
+  int tot;
+  const int above = tk_scan(s, sm, &tot);
+  if (above < want && want <= above + s) {
+    int cum = above;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (cum < want && want <= cum + c[i]) {
+        sm.bcast[0] = NB - 1 - PER * tid - i;
+        sm.bcast[1] = want - cum;
+      }
+      cum += c[i];
+    }
+  }
+  __syncthreads();
+  *digit = (uint32_t)sm.bcast[0];
+  *rem = sm.bcast[1];
+  __syncthreads();
+}
+
+// The key bits fixed by the first n_pass passes, their mask, and the rank
+// (1-based) of the k-th largest key among the keys that carry them.
+__device__ void tk_prefix(const TopkReq& st, int k, int n_pass, TkSmem& sm, uint32_t* prefix,
+                          uint32_t* mask, int* rem) {
+  uint32_t pf = 0, mk = 0, d;
+  int want = k;
+  if (n_pass > 0) {
+    tk_pick<TK_BINS0>(st.hist0, want, sm, &d, &want);
+    pf |= d << 21;
+    mk |= 0x7ffu << 21;
+  }
+  if (n_pass > 1) {
+    tk_pick<TK_BINS1>(st.hist1, want, sm, &d, &want);
+    pf |= d << 10;
+    mk |= 0x7ffu << 10;
+  }
+  if (n_pass > 2) {
+    tk_pick<TK_BINS2>(st.hist2, want, sm, &d, &want);
+    pf |= d;
+    mk |= 0x3ffu;
+  }
+  *prefix = pf;
+  *mask = mk;
+  *rem = want;
+}
+
+__device__ __forceinline__ int tk_budget(const int32_t* k_sel, const TopkReq& st, int r) {
+  return min(max(k_sel[r], 0), st.n_cand);
+}
+
+// Clears the per-request records.  A request with no tokens gets its padded
+// outputs here (no chunk of it exists).
+__global__ __launch_bounds__(TK_THREADS) void tk_init(TopkReq* __restrict__ st, int n_req,
+                                                      const int32_t* __restrict__ seq_start,
+                                                      const int32_t* __restrict__ k_sel,
+                                                      const int32_t* __restrict__ sq_start,
+                                                      int32_t* __restrict__ sel_rows,
+                                                      int32_t* __restrict__ act_rows) {
   const int r = blockIdx.x;
-  const int tid = threadIdx.x, w = tid >> 6;
-  const int t0 = seq_start[r], t1 = seq_start[r + 1];
+  uint32_t* wd = reinterpret_cast<uint32_t*>(&st[r]);
+  for (int i = threadIdx.x; i < (int)(sizeof(TopkReq) / 4); i += TK_THREADS) wd[i] = 0u;
+  if (seq_start[r + 1] > seq_start[r]) return;
   int sel_off = 0;
   for (int i = 0; i < r; ++i) sel_off += max(k_sel[i], 0);
   const int k_req = max(k_sel[r], 0);
-
-  // Every loop below visits the request's tokens in batches of TK_BATCH per
-  // thread (token t0 + tid + TK_THREADS * (b + u)), issuing all the batch's
-  // loads before using any of them: a single workgroup would otherwise pay
-  // one memory round trip per element per thread.
-  constexpr int U = TK_BATCH;
-  const int n = t1 - t0;
-  const int n_rounds = (n + TK_THREADS - 1) / TK_THREADS;
-
-  // pass 0: scores (fixed-order sum of the partial rows) and candidate count
-  const float* src = partial;
-  if (n_parts > 1 || scores != partial) {
-    for (int b = 0; b < n_rounds; b += U) {
-      float acc[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) acc[u] = 0.f;
-      for (int p = 0; p < n_parts; ++p) {
-        float v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int j = t0 + tid + TK_THREADS * (b + u);
-          v[u] = j < t1 ? partial[(size_t)p * n_tok + j] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) acc[u] += v[u];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = t0 + tid + TK_THREADS * (b + u);
-        if (j < t1) scores[j] = acc[u];
-      }
-    }
-    src = scores;
-    __threadfence_block();
-    __syncthreads();
+  for (int i = threadIdx.x; i < k_req; i += TK_THREADS) {
+    sel_rows[sel_off + i] = -1;
+    if (act_rows) act_rows[sq_start[r] + sel_off + i] = -1;
   }
-  // key and class of the batch starting at round b (class 2 past the end)
-  auto load_batch = [&](int b, uint32_t (&key)[U], int (&cls)[U]) __attribute__((always_inline)) {
-    float sv[U];
+}
+
+// Pass 0: the scores (fixed-order sum of the partial rows), the candidate
+// count and the histogram of key bits 31-21.
+__global__ __launch_bounds__(TK_THREADS) void tk_pass0(
+    const float* __restrict__ partial, int n_parts, int n_tok, const uint8_t* __restrict__ tok_class,
+    const int32_t* __restrict__ seq_start, int n_req, const int32_t* __restrict__ k_sel,
+    float* __restrict__ scores, TopkReq* __restrict__ st) {
+  __shared__ TkSmem sm;
+  int r, first;
+  if (!tk_chunk(seq_start, n_req, blockIdx.x, r, first)) return;
+  const int tid = threadIdx.x;
+  const int t1 = seq_start[r + 1];
+  const int j0 = seq_start[r] + (blockIdx.x - first) * TK_CHUNK + TK_PER * tid;
+  const bool sum = n_parts > 1 || scores != partial;
+  float sc[TK_PER];
+  int cls[TK_PER];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = t0 + tid + TK_THREADS * (b + u);
-      cls[u] = j < t1 ? (int)tok_class[j] : 2;
-      sv[u] = j < t1 ? src[j] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) key[u] = cls[u] == 0 ? order_key(sv[u]) : 0u;
-  };
-  int my_cand = 0;
-  for (int b = 0; b < n_rounds; b += U) {
-    uint32_t key[U];
-    int cls[U];
-    load_batch(b, key, cls);
-#pragma unroll
-    for (int u = 0; u < U; ++u) my_cand += cls[u] == 0;
+  for (int u = 0; u < TK_PER; ++u) {
+    const int j = j0 + u;
+    cls[u] = j < t1 ? (int)tok_class[j] : 2;
+    sc[u] = 0.f;
   }
+  if (sum) {
+    for (int p = 0; p < n_parts; ++p)
+#pragma unroll
+      for (int u = 0; u < TK_PER; ++u)
+        if (j0 + u < t1) sc[u] += partial[(size_t)p * n_tok + j0 + u];
+#pragma unroll
+    for (int u = 0; u < TK_PER; ++u)
+      if (j0 + u < t1) scores[j0 + u] = sc[u];
+  } else {
+#pragma unroll
+    for (int u = 0; u < TK_PER; ++u)
+      if (j0 + u < t1) sc[u] = partial[j0 + u];
+  }
+  for (int i = tid; i < TK_BINS0; i += TK_THREADS) sm.hist[i] = 0u;
+  __syncthreads();
+  const bool need = k_sel[r] > 0;
+  int cand = 0;
+#pragma unroll
+  for (int u = 0; u < TK_PER; ++u)
+    if (cls[u] == 0) {
+      ++cand;
+      if (need) atomicAdd(&sm.hist[order_key(sc[u]) >> 21], 1u);
+    }
   int n_cand;
-  block_scan(my_cand, sm, &n_cand);
-  const int k = min(k_req, n_cand);
+  tk_scan(cand, sm, &n_cand);                  // also orders the LDS histogram updates
+  if (tid == 0 && n_cand) atomicAdd(&st[r].n_cand, n_cand);
+  if (need)
+    for (int i = tid; i < TK_BINS0; i += TK_THREADS)
+      if (sm.hist[i]) atomicAdd(&st[r].hist0[i], sm.hist[i]);
+}
 
-  // radix select of the k-th largest key
-  uint32_t prefix = 0, pmask = 0;
-  int remaining = k;
-  if (k > 0) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      for (int i = tid; i < TK_WAVES * 256; i += TK_THREADS) (&sm.hist[0][0])[i] = 0;
-      __syncthreads();
-      for (int b = 0; b < n_rounds; b += U) {
-        uint32_t key[U];
-        int cls[U];
-        load_batch(b, key, cls);
+// Passes 1 and 2: histogram of key bits 20-10 (P = 1) or 9-0 (P = 2) of the
+// candidates whose higher bits match the digits chosen so far.
+template <int P>
+__global__ __launch_bounds__(TK_THREADS) void tk_pass(const float* __restrict__ src,
+                                                      const uint8_t* __restrict__ tok_class,
+                                                      const int32_t* __restrict__ seq_start, int n_req,
+                                                      const int32_t* __restrict__ k_sel,
+                                                      TopkReq* __restrict__ st) {
+  __shared__ TkSmem sm;
+  int r, first;
+  if (!tk_chunk(seq_start, n_req, blockIdx.x, r, first)) return;
+  const int k = tk_budget(k_sel, st[r], r);
+  if (k == 0) return;                          // uniform across the workgroup
+  const int tid = threadIdx.x;
+  const int t1 = seq_start[r + 1];
+  const int j0 = seq_start[r] + (blockIdx.x - first) * TK_CHUNK + TK_PER * tid;
+  uint32_t prefix, mask;
+  int rem;
+  tk_prefix(st[r], k, P, sm, &prefix, &mask, &rem);
+  constexpr int NB = P == 1 ? TK_BINS1 : TK_BINS2;
+  constexpr int SHIFT = P == 1 ? 10 : 0;
+  for (int i = tid; i < NB; i += TK_THREADS) sm.hist[i] = 0u;
+  __syncthreads();
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (cls[u] == 0 && (key[u] & pmask) == prefix) atomicAdd(&sm.hist[w][(key[u] >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid < 256) {
-        uint32_t s = 0;
-        for (int i = 0; i < TK_WAVES; ++i) s += sm.hist[i][tid];
-        sm.hist[0][tid] = s;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int cum = 0, dsel = 0;
-        for (int d = 255; d >= 0; --d) {
-          const int c = (int)sm.hist[0][d];
-          if (cum + c >= remaining) { dsel = d; break; }
-          cum += c;
-        }
-        sm.bcast[0] = dsel;
-        sm.bcast[1] = remaining - cum;
-      }
-      __syncthreads();
-      prefix |= (uint32_t)sm.bcast[0] << shift;
-      pmask |= 0xffu << shift;
-      remaining = sm.bcast[1];
-      __syncthreads();
+  for (int u = 0; u < TK_PER; ++u) {
+    const int j = j0 + u;
+    if (j < t1 && tok_class[j] == 0) {
+      const uint32_t key = order_key(src[j]);
+      if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> SHIFT) & (NB - 1)], 1u);
     }
   }
-  const uint32_t thr = prefix;       // key of the k-th largest candidate
-  const int need_eq = remaining;     // how many keys equal to thr to take
+  __syncthreads();
+  uint32_t* gh = P == 1 ? st[r].hist1 : st[r].hist2;
+  for (int i = tid; i < NB; i += TK_THREADS)
+    if (sm.hist[i]) atomicAdd(&gh[i], sm.hist[i]);
+}
 
-  // in-order compaction, one round of TK_THREADS tokens at a time (a batch
-  // of rounds loaded together)
+// Per chunk: candidates above / equal to the k-th largest key, class-1 tokens.
+__global__ __launch_bounds__(TK_THREADS) void tk_count(const float* __restrict__ src,
+                                                       const uint8_t* __restrict__ tok_class,
+                                                       const int32_t* __restrict__ seq_start, int n_req,
+                                                       const int32_t* __restrict__ k_sel,
+                                                       const TopkReq* __restrict__ st,
+                                                       TopkChunk* __restrict__ cnt) {
+  __shared__ TkSmem sm;
+  int r, first;
+  if (!tk_chunk(seq_start, n_req, blockIdx.x, r, first)) return;
+  const int k = tk_budget(k_sel, st[r], r);
+  const int tid = threadIdx.x;
+  const int t1 = seq_start[r + 1];
+  const int j0 = seq_start[r] + (blockIdx.x - first) * TK_CHUNK + TK_PER * tid;
+  uint32_t thr = 0, mask = 0;
+  int rem = 0;
+  if (k > 0) tk_prefix(st[r], k, 3, sm, &thr, &mask, &rem);
+  int ge = 0, n1 = 0;                           // gt | eq << 16 (each <= TK_CHUNK); class-1 count
+#pragma unroll
+  for (int u = 0; u < TK_PER; ++u) {
+    const int j = j0 + u;
+    if (j >= t1) continue;
+    const int c = tok_class[j];
+    n1 += c == 1;
+    if (c == 0 && k > 0) {
+      const uint32_t key = order_key(src[j]);
+      ge += key > thr ? 1 : (key == thr ? 1 << 16 : 0);
+    }
+  }
+  int ge_tot, n1_tot;
+  tk_scan(ge, sm, &ge_tot);
+  tk_scan(n1, sm, &n1_tot);
+  if (tid == 0) cnt[blockIdx.x] = TopkChunk{ge_tot & 0xffff, ge_tot >> 16, n1_tot, 0};
+}
+
+// Ordered output: each chunk's selected tokens (and active rows) follow
+// those of the request's earlier chunks.
+__global__ __launch_bounds__(TK_THREADS) void tk_emit(
+    const float* __restrict__ src, const uint8_t* __restrict__ tok_class,
+    const int32_t* __restrict__ seq_start, int n_req, const int32_t* __restrict__ k_sel,
+    const int32_t* __restrict__ sq_start, const TopkReq* __restrict__ st,
+    const TopkChunk* __restrict__ cnt, int32_t* __restrict__ sel_rows, int32_t* __restrict__ act_rows) {
+  __shared__ TkSmem sm;
+  int r, first;
+  if (!tk_chunk(seq_start, n_req, blockIdx.x, r, first)) return;
+  const int k = tk_budget(k_sel, st[r], r);
+  const int k_req = max(k_sel[r], 0);
+  const int tid = threadIdx.x;
+  const int t0 = seq_start[r], t1 = seq_start[r + 1];
+  const int ci = blockIdx.x - first;
+  const int j0 = t0 + ci * TK_CHUNK + TK_PER * tid;
+  uint32_t thr = 0, mask = 0;
+  int need_eq = 0;
+  if (k > 0) tk_prefix(st[r], k, 3, sm, &thr, &mask, &need_eq);
+  int sel_off = 0;
+  for (int i = 0; i < r; ++i) sel_off += max(k_sel[i], 0);
   const int act_off = act_rows ? sq_start[r] + sel_off : 0;
-  int base_eq = 0, base_sel = 0, base_act = 0;
-  for (int b = 0; b < n_rounds; b += U) {
-    uint32_t key[U];
-    int cls[U];
-    load_batch(b, key, cls);
+
+  // Selected and active counts of the earlier chunks, in chunk order.
+  int eq_before = 0, sel_before = 0, act_before = 0;
+  for (int c0 = 0; c0 < ci; c0 += TK_THREADS) {
+    const int c = c0 + tid;
+    TopkChunk e = {0, 0, 0, 0};
+    if (c < ci) e = cnt[first + c];
+    int eq_tot;
+    const int eq_ex = eq_before + tk_scan(e.eq, sm, &eq_tot);
+    const int take_eq = min(max(need_eq - eq_ex, 0), e.eq);
+    const int s = e.gt + take_eq;
+    int s_tot, a_tot;
+    tk_scan(s, sm, &s_tot);
+    tk_scan(s + e.c1, sm, &a_tot);
+    eq_before += eq_tot;
+    sel_before += s_tot;
+    act_before += a_tot;
+  }
+
+  // This chunk: flags of the thread's tokens, then two ordered scans.
+  bool gt[TK_PER], eq[TK_PER], c1[TK_PER];
+  int n_eq = 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (b + u >= n_rounds) break;                 // uniform across the workgroup
-      const int j = t0 + tid + TK_THREADS * (b + u);
-      const bool cand = cls[u] == 0 && k > 0;
-      const bool gt = cand && key[u] > thr;
-      const bool eq = cand && key[u] == thr;
-      int tot_eq;
-      const int eq_rank = base_eq + block_scan(eq ? 1 : 0, sm, &tot_eq);
-      const bool sel = gt || (eq && eq_rank < need_eq);
-      const bool act = sel || cls[u] == 1;
-      int tot_pk;
-      const int pk = block_scan((sel ? 1 : 0) | (act ? 1 << 16 : 0), sm, &tot_pk);
-      if (sel) sel_rows[sel_off + base_sel + (pk & 0xffff)] = j;
-      if (act && act_rows) act_rows[act_off + base_act + (pk >> 16)] = j;
-      base_eq += tot_eq;
-      base_sel += tot_pk & 0xffff;
-      base_act += tot_pk >> 16;
+  for (int u = 0; u < TK_PER; ++u) {
+    const int j = j0 + u;
+    const int c = j < t1 ? (int)tok_class[j] : 2;
+    const uint32_t key = c == 0 ? order_key(src[j]) : 0u;
+    gt[u] = c == 0 && k > 0 && key > thr;
+    eq[u] = c == 0 && k > 0 && key == thr;
+    c1[u] = c == 1;
+    n_eq += eq[u];
+  }
+  int eq_tot;
+  int eq_rank = eq_before + tk_scan(n_eq, sm, &eq_tot);
+  bool sel[TK_PER];
+  int n_sel = 0, n_act = 0;
+#pragma unroll
+  for (int u = 0; u < TK_PER; ++u) {
+    sel[u] = gt[u] || (eq[u] && eq_rank < need_eq);
+    eq_rank += eq[u];
+    n_sel += sel[u];
+    n_act += sel[u] || c1[u];
+  }
+  int pk_tot;
+  const int pk = tk_scan(n_sel | (n_act << 16), sm, &pk_tot);
+  int ps = sel_before + (pk & 0xffff), pa = act_before + (pk >> 16);
+#pragma unroll
+  for (int u = 0; u < TK_PER; ++u) {
+    if (sel[u]) sel_rows[sel_off + ps++] = j0 + u;
+    if (act_rows && (sel[u] || c1[u])) act_rows[act_off + pa++] = j0 + u;
+  }
+  // The request's last chunk pads budgets larger than the candidate count.
+  const int n_chunks = (t1 - t0 + TK_CHUNK - 1) / TK_CHUNK;
+  if (ci == n_chunks - 1) {
+    const int act_total = act_before + (pk_tot >> 16);
+    for (int i = k + tid; i < k_req; i += TK_THREADS) {
+      sel_rows[sel_off + i] = -1;
+      if (act_rows) act_rows[act_off + act_total + (i - k)] = -1;
     }
   }
-  // budgets larger than the candidate count: pad with -1
-  for (int i = k + tid; i < k_req; i += TK_THREADS) sel_rows[sel_off + i] = -1;
-  if (act_rows)
-    for (int i = base_act + tid; i < base_act + (k_req - k); i += TK_THREADS) act_rows[act_off + i] = -1;
 }
 
 }  // namespace
 
+// Chunks of the top-k grid (>= the sum of the per-request chunk counts).
+static int topk_chunks(int n_tok, int n_req) { return n_tok / TK_CHUNK + n_req + 1; }
+
 size_t topk_ws_bytes(int n_tok, int n_req) {
-  (void)n_req;
-  return align256((size_t)n_tok * sizeof(float));
+  return align256((size_t)n_req * sizeof(TopkReq)) +
+         align256((size_t)topk_chunks(n_tok, n_req) * sizeof(TopkChunk));
 }
 
 size_t select_ws_bytes(const sx_dims& d, int n_tok, int n_sq, int n_req) {
   return align256((size_t)score_parts(d, n_tok, n_req) * n_tok * sizeof(float))  // partial scores
          + align256((size_t)n_tok * sizeof(float))                // scores if caller passes none
          + align256((size_t)n_sq * d.n_q_heads * sizeof(float))   // probe LSE
-         + attn_ws_bytes(d, n_sq, n_req, false);                   // probe work list
+         + std::max({attn_ws_bytes(d, n_sq, n_req, false),         // probe work list, then
+                     scores_gather_bytes(d, n_sq),                 // the gathered Sparse-Q rows,
+                     topk_ws_bytes(n_tok, n_req)});                // then the top-k records
 }
 
 // Key tiles of the score grid (>= the sum of the per-request tile counts).
@@ -427,17 +767,34 @@ int score_parts(const sx_dims& d, int n_tok, int n_req) {
   return (long long)score_tiles(n_tok, n_req) * d.n_kv_heads < 512 ? d.n_q_heads : d.n_kv_heads;
 }
 
+size_t scores_gather_bytes(const sx_dims& d, int n_sq) {
+  if (d.dtype != SX_BF16) return 0;
+  return align256((size_t)n_sq * d.n_q_heads * 128 * sizeof(uint16_t)) +
+         align256((size_t)n_sq * d.n_q_heads * sizeof(float)) + align256((size_t)n_sq * sizeof(int32_t));
+}
+
 sx_status launch_scores(const sx_dims& dims, const sx_layout& lay, const void* q,
                         const int32_t* q_index, const int32_t* sq_rows, const int32_t* sq_start,
                         int n_sq, const float* lse, const int32_t* lse_index,
-                        const sx_pages& kv, float* partial, hipStream_t stream) {
-  (void)n_sq;
+                        const sx_pages& kv, float* partial, void* gather_ws, hipStream_t stream) {
   const int hq = dims.n_q_heads, hkv = dims.n_kv_heads, d = dims.head_dim;
   if (dims.dtype == SX_BF16) {
+    char* p = static_cast<char*>(gather_ws);
+    uint16_t* q_g = reinterpret_cast<uint16_t*>(p);
+    p += align256((size_t)n_sq * hq * 128 * sizeof(uint16_t));
+    float* lse2_g = reinterpret_cast<float*>(p);
+    p += align256((size_t)n_sq * hq * sizeof(float));
+    int32_t* pos_g = reinterpret_cast<int32_t*>(p);
+    if (n_sq > 0) {
+      sq_gather<<<n_sq, 256, 0, stream>>>((const uint16_t*)q, q_index, lse, lse_index, sq_rows, sq_start,
+                                          lay.seq_start, lay.n_req, n_sq, hq, q_g, lse2_g, pos_g);
+      const sx_status st = check_launch("sx_select_topk (Sparse-Q gather)");
+      if (st != SX_OK) return st;
+    }
     const int parts = score_parts(dims, lay.n_tok, lay.n_req);
     scores_bf16<<<dim3(score_tiles(lay.n_tok, lay.n_req), parts), 256, 0, stream>>>(
-        (const uint16_t*)q, q_index, sq_rows, sq_start, lse, lse_index, lay, kv.n_pages,
-        (const uint16_t*)kv.k, hq, hkv, partial, kLog2e / sqrtf((float)d), hq / parts);
+        q_g, lse2_g, pos_g, sq_start, lay, kv.n_pages, (const uint16_t*)kv.k, hq, hkv, partial,
+        kLog2e / sqrtf((float)d), hq / parts, n_sq);
   } else {
     dim3 grid((lay.n_tok + 255) / 256, hkv);
     const float scale = 1.f / sqrtf((float)d);
@@ -457,10 +814,20 @@ sx_status launch_topk(const float* partial, int n_parts, const uint8_t* tok_clas
                       const int32_t* seq_start, int n_req, int n_tok, const int32_t* k_sel,
                       const int32_t* sq_start, int32_t* sel_rows, int32_t* act_rows,
                       float* scores_out, void* ws, hipStream_t stream) {
-  (void)ws;
   if (n_req == 0) return SX_OK;
-  topk_kernel<<<n_req, TK_THREADS, 0, stream>>>(partial, n_parts, n_tok, tok_class, seq_start,
-                                                k_sel, sq_start, sel_rows, act_rows, scores_out);
+  TopkReq* st = static_cast<TopkReq*>(ws);
+  TopkChunk* cnt = reinterpret_cast<TopkChunk*>(static_cast<char*>(ws) +
+                                                align256((size_t)n_req * sizeof(TopkReq)));
+  const int nc = topk_chunks(n_tok, n_req);
+  const float* src = (n_parts > 1 || scores_out != partial) ? scores_out : partial;
+  tk_init<<<n_req, TK_THREADS, 0, stream>>>(st, n_req, seq_start, k_sel, sq_start, sel_rows, act_rows);
+  tk_pass0<<<nc, TK_THREADS, 0, stream>>>(partial, n_parts, n_tok, tok_class, seq_start, n_req, k_sel,
+                                           scores_out, st);
+  tk_pass<1><<<nc, TK_THREADS, 0, stream>>>(src, tok_class, seq_start, n_req, k_sel, st);
+  tk_pass<2><<<nc, TK_THREADS, 0, stream>>>(src, tok_class, seq_start, n_req, k_sel, st);
+  tk_count<<<nc, TK_THREADS, 0, stream>>>(src, tok_class, seq_start, n_req, k_sel, st, cnt);
+  tk_emit<<<nc, TK_THREADS, 0, stream>>>(src, tok_class, seq_start, n_req, k_sel, sq_start, st, cnt,
+                                          sel_rows, act_rows);
   return check_launch("top-k");
 }
 

@@ -68,10 +68,12 @@ sx_status decode_scratch(void** ptr);
 int score_parts(const sx_dims& d, int n_tok, int n_req);
 
 // Partial attention-mass scores of the Sparse-Q rows, per score_parts row.
+// gather_ws: scores_gather_bytes(dims, n_sq) bytes for the bf16 path.
+size_t scores_gather_bytes(const sx_dims& d, int n_sq);
 sx_status launch_scores(const sx_dims& dims, const sx_layout& lay, const void* q,
                         const int32_t* q_index, const int32_t* sq_rows, const int32_t* sq_start,
                         int n_sq, const float* lse, const int32_t* lse_index,
-                        const sx_pages& kv, float* partial, hipStream_t stream);
+                        const sx_pages& kv, float* partial, void* gather_ws, hipStream_t stream);
 
 // Top-k on the sum over `n_parts` partial score rows ([n_parts][n_tok]).
 sx_status launch_topk(const float* partial, int n_parts, const uint8_t* tok_class,

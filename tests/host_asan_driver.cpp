@@ -50,7 +50,8 @@ sx_status launch_decode(const sx_dims&, const sx_layout&, const void*, const sx_
                         void*, hipStream_t) { reached("launch_decode"); }
 sx_status launch_scores(const sx_dims&, const sx_layout&, const void*, const int32_t*, const int32_t*,
                         const int32_t*, int, const float*, const int32_t*, const sx_pages&, float*,
-                        hipStream_t) { reached("launch_scores"); }
+                        void*, hipStream_t) { reached("launch_scores"); }
+size_t scores_gather_bytes(const sx_dims&, int) { return 0; }
 sx_status launch_topk(const float*, int, const uint8_t*, const int32_t*, int, int, const int32_t*,
                       const int32_t*, int32_t*, int32_t*, float*, void*, hipStream_t) { reached("launch_topk"); }
 sx_status launch_mfma_peak(int, int, int, float*, hipStream_t) { reached("launch_mfma_peak"); }

@@ -466,6 +466,87 @@ def test_topk_bit_exact_adversarial():
         off += ks[r]
 
 
+def test_topk_many_chunks_ties_and_padding():
+    """The radix select runs one workgroup per 1,024-token chunk: ties at
+    the threshold that straddle chunk boundaries must still go to the lowest
+    token ids, budgets above the candidate count are padded with -1 (also
+    for a request with no tokens), and a 70K-token request spans 69 chunks."""
+    say("[topk] many chunks, ties, padding")
+    rng = np.random.default_rng(67)
+    lens = [70000, 0, 1500, 3000, 1025]
+    seq = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    n_tok = int(seq[-1])
+    parts = [rng.integers(0, 6, 70000).astype(np.float32) / 8,      # six values: long tie runs
+             np.zeros(0, np.float32),
+             rng.standard_normal(1500).astype(np.float32),
+             np.where(rng.random(3000) < 0.999, 1.0, 3.0).astype(np.float32),
+             np.full(1025, -2.5, np.float32)]
+    scores = np.concatenate(parts)
+    tok_class = (rng.random(n_tok) < 0.1).astype(np.uint8)
+    tok_class[seq[2]:seq[3]] = np.where(rng.random(1500) < 0.9, 2, tok_class[seq[2]:seq[3]])
+    n_cand = [int(np.sum(tok_class[seq[r]:seq[r + 1]] == 0)) for r in range(len(lens))]
+    k_req = [31000, 5, n_cand[2] + 40, 2999, 1000]
+    sel = torch.full((sum(k_req),), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(L.sx_workspace_bytes(L.SX_OP_TOPK, LY.make_dims(SHAPES["llama"]), n_tok, 0, len(lens)),
+                     dtype=torch.uint8, device=DEV)
+    L.sx_topk(torch.from_numpy(scores).to(DEV), torch.from_numpy(tok_class).to(DEV),
+              torch.from_numpy(seq).to(DEV), len(lens), n_tok,
+              torch.from_numpy(np.array(k_req, np.int32)).to(DEV), sel, ws)
+    torch.cuda.synchronize()
+    got = sel.cpu().numpy()
+    off = 0
+    for r in range(len(lens)):
+        k = min(k_req[r], n_cand[r])
+        sc = scores[seq[r]:seq[r + 1]].astype(np.float64)
+        cand = np.flatnonzero(tok_class[seq[r]:seq[r + 1]] == 0)
+        ref = oracle.select_topk(sc, cand, k)
+        seg = got[off:off + k_req[r]]
+        assert np.array_equal(seg[:k] - seq[r], ref), f"request {r}"
+        assert np.all(seg[k:] == -1), f"request {r}: padding"
+        say(f"  req {r}: len {lens[r]} candidates {n_cand[r]} budget {k_req[r]} -> {k} selected")
+        off += k_req[r]
+
+
+def test_select_padding_of_active_rows():
+    """sx_select_topk with budgets above the candidate count: the selection
+    and the active rows (Sparse-Q rows merged with the selection) are padded
+    with -1 after their valid entries."""
+    dims = SHAPES["llama"]
+    lens = [900, 0, 2100]
+    say(f"[select] padding lens={lens}")
+    rng, seq, pool, kh, vh, bt = _attn_inputs(dims, lens, 71)
+    cd = LY.make_dims(dims)
+    n_tok = int(seq[-1])
+    lay = LY.DeviceLayout(np.asarray(seq, np.int32), bt, LY.rope_table(dims.theta, dims.head_dim, 4096, DEV), DEV)
+    sq_rows = np.r_[seq[0] + 880:seq[0] + 900, seq[2] + 2000:seq[2] + 2100].astype(np.int32)
+    sq_start = np.array([0, 20, 20, 120], np.int32)
+    tok_class = np.where(rng.random(n_tok) < 0.5, 2, 0).astype(np.uint8)
+    tok_class[sq_rows] = 1
+    n_cand = [int(np.sum(tok_class[seq[r]:seq[r + 1]] == 0)) for r in range(len(lens))]
+    k_req = np.array([n_cand[0] + 7, 3, 50], np.int32)
+    q = (rng.standard_normal((len(sq_rows), dims.n_q_heads, dims.head_dim)) * 0.5).astype(np.float32)
+    sel = torch.full((int(k_req.sum()),), -7, dtype=torch.int32, device=DEV)
+    act = torch.full((len(sq_rows) + int(k_req.sum()),), -7, dtype=torch.int32, device=DEV)
+    ws = LY.workspace(L.SX_OP_SELECT, cd, n_tok, len(sq_rows), len(lens), DEV)
+    L.sx_select_topk(cd, lay.struct, torch.from_numpy(q).to(torch.bfloat16).to(DEV), None,
+                     torch.from_numpy(sq_rows).to(DEV), torch.from_numpy(sq_start).to(DEV), len(sq_rows),
+                     None, pool.struct(), torch.from_numpy(tok_class).to(DEV), torch.from_numpy(k_req).to(DEV),
+                     sel, act, None, ws)
+    torch.cuda.synchronize()
+    selg, actg = sel.cpu().numpy(), act.cpu().numpy()
+    off = 0
+    for r in range(len(lens)):
+        k = min(int(k_req[r]), n_cand[r])
+        s = selg[off:off + k_req[r]]
+        assert np.all(np.diff(s[:k]) > 0) and np.all(s[k:] == -1), f"request {r}: selection {s}"
+        n_sq = sq_start[r + 1] - sq_start[r]
+        a = actg[sq_start[r] + off:sq_start[r] + off + n_sq + k_req[r]]
+        assert np.array_equal(a[:n_sq + k], np.union1d(sq_rows[sq_start[r]:sq_start[r + 1]], s[:k])), r
+        assert np.all(a[n_sq + k:] == -1), f"request {r}: active rows {a}"
+        off += k_req[r]
+    assert np.all(selg != -7) and np.all(actg != -7)
+
+
 def test_sparse_attention_rows_far_apart():
     """A handful of active rows at the start and at the end of a long
     request share query tiles: the tiles are split on the key grid, and for
