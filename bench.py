@@ -485,10 +485,12 @@ def main():
     }
     # every kernel of the sparse layer (and the full layer) against its roofline,
     # per launch; the selection's work is the QK^T of the Sparse-Q rows over
-    # their key prefixes, once for the LSE probe and once for the scores
+    # their key prefixes for the scores, plus the same again for the LSE probe
+    # when the selection runs inside layer 0 (t = 0; at a boundary t > 0 the
+    # LSE comes from layer t-1's full attention)
     sq_tok = np.asarray(run.plan["sq_rows"], dtype=np.int64)
     sq = sq_tok - seq_h[np.searchsorted(seq_h, sq_tok, side="right") - 1]
-    sel_flops = 2 * (2.0 * dims.head_dim * dims.n_q_heads * float(np.sum(sq + 1)))
+    sel_flops = (2 if t == 0 else 1) * (2.0 * dims.head_dim * dims.n_q_heads * float(np.sum(sq + 1)))
     full_rec_flops = 2.0 * T * dims.qkv_rows * dims.hidden
     rate = lambda work, ms, unit: round(work / (ms * 1e-3) / unit, 1) if ms else None
     out["kernels"] = {

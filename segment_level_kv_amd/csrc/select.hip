@@ -552,10 +552,26 @@ __global__ __launch_bounds__(TK_THREADS) void tk_pass0(
     sc[u] = 0.f;
   }
   if (sum) {
-    for (int p = 0; p < n_parts; ++p)
+    // eight partial rows loaded per round (unconditionally, at clamped
+    // indices, so the loads are not serialised by branches), then added in
+    // row order
+    constexpr int PB = 8;
+    for (int p0 = 0; p0 < n_parts; p0 += PB) {
+      float v[PB][TK_PER];
 #pragma unroll
-      for (int u = 0; u < TK_PER; ++u)
-        if (j0 + u < t1) sc[u] += partial[(size_t)p * n_tok + j0 + u];
+      for (int p = 0; p < PB; ++p)
+#pragma unroll
+        for (int u = 0; u < TK_PER; ++u)
+          v[p][u] = partial[(size_t)min(p0 + p, n_parts - 1) * n_tok + min(j0 + u, t1 - 1)];
+#pragma unroll
+      for (int p = 0; p < PB; ++p)
+#pragma unroll
+        for (int u = 0; u < TK_PER; ++u)
+          if (p0 + p < n_parts) sc[u] += v[p][u];
+    }
+#pragma unroll
+    for (int u = 0; u < TK_PER; ++u)
+      if (j0 + u >= t1) sc[u] = 0.f;
 #pragma unroll
     for (int u = 0; u < TK_PER; ++u)
       if (j0 + u < t1) scores[j0 + u] = sc[u];
