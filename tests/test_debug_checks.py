@@ -141,3 +141,30 @@ def test_debug_reports_bad_rows_and_positions(monkeypatch):
     torch.cuda.synchronize()
     assert torch.equal(pool.k.view(torch.int16), before.view(torch.int16))
     assert bool((o == 5.0).all())
+
+
+def test_debug_reports_bad_selection_rows(monkeypatch):
+    """sx_select_topk checks its Sparse-Q row list (grouped by request,
+    ascending, inside the request) and the layout before any kernel runs."""
+    monkeypatch.setenv("SX_DEBUG", "1")
+    pool, bt, lay, _ = _setup()
+    cd = LY.make_dims(D)
+    n_sq = 4
+    q = torch.randn((n_sq, D.n_q_heads, D.head_dim), device=DEV).to(torch.bfloat16)
+    tok_class = torch.zeros(T, dtype=torch.uint8, device=DEV)
+    k_sel = torch.tensor([10], dtype=torch.int32, device=DEV)
+    sel = torch.full((10,), -7, dtype=torch.int32, device=DEV)
+    act = torch.full((10 + n_sq,), -7, dtype=torch.int32, device=DEV)
+    ws = LY.workspace(L.SX_OP_SELECT, cd, T, n_sq, 1, DEV)
+    sq_start = torch.tensor([0, n_sq], dtype=torch.int32, device=DEV)
+    for rows_h, what in [([96, 97, 98, T + 3], "row past the request"), ([96, 95, 98, 99], "rows out of order")]:
+        say(f"[debug] selection: {what}")
+        sq_rows = torch.tensor(rows_h, dtype=torch.int32, device=DEV)
+        _expect_edevice("row list", L.sx_select_topk, cd, lay.struct, q, None, sq_rows, sq_start, n_sq, None,
+                        pool.struct(), tok_class, k_sel, sel, act, None, ws)
+    bad_pool, _, bad_lay, _ = _setup(bad_page=True)
+    sq_rows = torch.tensor([96, 97, 98, 99], dtype=torch.int32, device=DEV)
+    _expect_edevice("block-table page id", L.sx_select_topk, cd, bad_lay.struct, q, None, sq_rows, sq_start,
+                    n_sq, None, bad_pool.struct(), tok_class, k_sel, sel, act, None, ws)
+    torch.cuda.synchronize()
+    assert bool((sel == -7).all()) and bool((act == -7).all())

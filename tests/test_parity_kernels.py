@@ -19,8 +19,8 @@ import oracle
 from segment_level_kv_amd import _lib as L
 from segment_level_kv_amd import layer as LY
 from segment_level_kv_amd import synth
-from tests.gpu_util import (BF16_STEP_REL, assert_close_bf16, assert_close_f32, bf16_ulps, say,
-                            selection_contract)
+from tests.gpu_util import (BF16_STEP_REL, assert_close_bf16, assert_close_f32, assert_o_bf16, bf16_ulps,
+                            say, selection_contract)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -357,19 +357,25 @@ def test_full_attention_parity(shape, lens):
     lay = LY.DeviceLayout(seq, bt, LY.rope_table(dims.theta, dims.head_dim, 16, DEV), DEV)
     cd = LY.make_dims(dims)
     o = torch.zeros((n_tok, dims.n_q_heads * dims.head_dim), dtype=dt, device=DEV)
+    lse = torch.full((n_tok, dims.n_q_heads), 7.0, dtype=torch.float32, device=DEV)
     ws = LY.workspace(L.SX_OP_FULL_ATTN, cd, n_tok, n_tok, len(lens), DEV)
-    L.sx_full_attn(cd, lay.struct, torch.from_numpy(q).to(dt).to(DEV), pool.struct(), o, None, ws)
+    L.sx_full_attn(cd, lay.struct, torch.from_numpy(q).to(dt).to(DEV), pool.struct(), o, lse, ws)
     torch.cuda.synchronize()
     og = o.float().cpu().double().numpy()
+    lg = lse.cpu().double().numpy()
     for r in range(len(lens)):
         K, V = _logical(kh, vh, bt[r], 0, lens[r])
         sl = slice(seq[r], seq[r + 1])
-        ref, _ = oracle.causal_attention(q[sl], np.arange(lens[r]), K, V)
+        ref, lse_ref = oracle.causal_attention(q[sl], np.arange(lens[r]), K, V)
         ref = ref.reshape(len(ref), -1)
+        # the normaliser is fp32 on the GPU over the same stored q and K
+        lerr = float(np.max(np.abs(lg[sl] - lse_ref)))
+        assert lerr <= 1e-4, f"LSE req {r}: max abs err {lerr:.3g}"
         if dims.dtype == "bf16":
-            assert_close_bf16(og[sl], ref, what=f"O req {r}")
+            err = assert_o_bf16(og[sl], ref, what=f"O req {r}")
         else:
-            assert_close_f32(og[sl], ref, what=f"O req {r}")
+            err = assert_close_f32(og[sl], ref, what=f"O req {r}")
+        say(f"  req {r}: O max err {err:.3g} LSE max abs err {lerr:.3g}")
 
 
 # ------------------------------------------------------------ probe + top-k --
