@@ -400,8 +400,8 @@ def main():
     # stream events around the whole section) per sparse layer
     t_layer_ms = sparse_wall_ms / n_sparse
     value = T / (t_layer_ms * 1e-3)
-    phase_sum_ms = (ph.get("realign", 0) + ph.get("recompute", 0) + ph.get("sparse_attn", 0)
-                    + ph.get("select", 0) + ph.get("attn_plan", 0)) / K / n_sparse
+    phase_sum_ms = (ph.get("realign", 0) + ph.get("recompute", 0) + ph.get("recompute_realign", 0)
+                    + ph.get("sparse_attn", 0) + ph.get("select", 0) + ph.get("attn_plan", 0)) / K / n_sparse
 
     # sparse attention roofline: unmasked MACs of QK^T and PV
     act = run.act_rows[:run.n_act].cpu().numpy().astype(np.int64)
@@ -422,6 +422,10 @@ def main():
     full_attn_ms = ph.get("full_attn", 0) / max(cnt.get("full_attn", 1), 1)
     full_attn_flops = 4.0 * dims.head_dim * dims.n_q_heads * (T * (T + 1) / 2)
     sel_ms = ph.get("select", 0) / max(cnt.get("select", 1), 1)
+    # layer l's recompute launch carrying layer l+1's realign (all sparse
+    # layers but the last); "realign" and "recompute" above are the first
+    # layer's realign and the last layer's recompute, each alone
+    rr_ms = ph.get("recompute_realign", 0) / max(cnt.get("recompute_realign", 1), 1)
     plan_ms = ph.get("attn_plan", 0) / max(cnt.get("attn_plan", 1), 1)
 
     out = {
@@ -467,6 +471,7 @@ def main():
         },
         "phases_ms_per_launch": {
             "realign": round(realign_ms, 4), "recompute_active": round(rec_ms, 4),
+            "recompute_active_with_next_realign": round(rr_ms, 4),
             "sparse_attn": round(attn_ms, 4), "select": round(sel_ms, 4), "attn_plan": round(plan_ms, 4),
             "full_recompute": round(full_rec_ms, 4), "full_attn": round(full_attn_ms, 4),
         },

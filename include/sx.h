@@ -324,6 +324,23 @@ sx_status sx_recompute_kv(const sx_dims *dims, const sx_layout *lay, const void 
                           const int32_t *rows, int32_t n_rows, const void *w_qkv,
                           const sx_pages *kv, void *q_out, void *stream);
 
+/* Steps 3 and 1 of two consecutive sparse layers in one call:
+ * sx_recompute_kv(dims, lay, x, rows, n_rows, w_qkv, kv, q_out) for layer l
+ * and sx_rope_realign(dims, lay, rsrc, rdst, jobs, n_jobs) for layer l+1's
+ * cache (§3.4 recomputation; §3.1 delta equation and §4.4 copy semantics),
+ * with the same results as the two calls in either order.  Layer l+1's
+ * realign only has to finish before its own recomputation, so when the
+ * projection's tiles leave compute units free (bf16, more than 64 rows) the
+ * realign jobs run on those units inside the same launch; otherwise the two
+ * are launched one after the other.  rdst must not share pages with kv (a
+ * different pool; the call rejects rdst == kv with SX_EINVAL, and partial
+ * overlaps are undefined).  Errors: those of the two calls. */
+sx_status sx_recompute_kv_realign(const sx_dims *dims, const sx_layout *lay, const void *x,
+                                  const int32_t *rows, int32_t n_rows, const void *w_qkv,
+                                  const sx_pages *kv, void *q_out, const sx_pages *rsrc,
+                                  const sx_pages *rdst, const sx_realign_job *jobs, int32_t n_jobs,
+                                  void *stream);
+
 /* Step 2 -- Sparse-Q scoring and top-k (§3.2 probe cost equation and the
  * paragraph after it: one score per token aggregated across heads; §3.3
  * first sentence: top-k per request).  For every token j of request r:

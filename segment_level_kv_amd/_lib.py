@@ -22,7 +22,8 @@ SX_OP_REALIGN, SX_OP_RECOMPUTE, SX_OP_SELECT, SX_OP_TOPK, SX_OP_SPARSE_ATTN, SX_
 
 EXPORTED = [
     "sx_rope_table", "sx_plan_layout", "sx_plan_realign", "sx_realign_jobs_bound",
-    "sx_workspace_bytes", "sx_rope_realign", "sx_recompute_kv", "sx_select_topk", "sx_topk",
+    "sx_workspace_bytes", "sx_rope_realign", "sx_recompute_kv", "sx_recompute_kv_realign", "sx_select_topk",
+    "sx_topk",
     "sx_sparse_attn", "sx_sparse_attn_plan", "sx_sparse_attn_run", "sx_full_attn", "sx_decode_attn", "sx_decode_attn_noalloc", "sx_mfma_peak_probe", "sx_last_error",
     "sx_virtual_hash", "sx_index_create", "sx_index_destroy", "sx_index_alloc", "sx_index_release",
     "sx_index_insert", "sx_index_lookup", "sx_index_remove", "sx_index_stats", "sx_plan_segments",
@@ -80,6 +81,7 @@ def lib():
             "sx_workspace_bytes": (Z, [I, P, I, I, I]),
             "sx_rope_realign": (I, [P, P, P, P, P, I, P]),
             "sx_recompute_kv": (I, [P, P, P, P, I, P, P, P, P]),
+            "sx_recompute_kv_realign": (I, [P, P, P, P, I, P, P, P, P, P, P, I, P]),
             "sx_select_topk": (I, [P, P, P, P, P, P, I, P, P, P, P, P, P, P, P, Z, P]),
             "sx_topk": (I, [P, P, P, I, I, P, P, P, Z, P]),
             "sx_sparse_attn": (I, [P, P, P, P, P, I, P, P, P, P, Z, P]),
@@ -304,6 +306,13 @@ def sx_recompute_kv(dims: Dims, lay: Layout, x, rows, n_rows: int, w_qkv, kv: Pa
                     stream=None):
     _check(lib().sx_recompute_kv(_ref(dims), _ref(lay), _ptr(x), _ptr(rows), n_rows, _ptr(w_qkv),
                                  _ref(kv), _ptr(q_out), _stream(stream)), "sx_recompute_kv")
+
+
+def sx_recompute_kv_realign(dims: Dims, lay: Layout, x, rows, n_rows: int, w_qkv, kv: Pages, q_out,
+                            rsrc: Pages, rdst: Pages, jobs, n_jobs: int, stream=None):
+    _check(lib().sx_recompute_kv_realign(_ref(dims), _ref(lay), _ptr(x), _ptr(rows), n_rows, _ptr(w_qkv),
+                                         _ref(kv), _ptr(q_out), _ref(rsrc), _ref(rdst), _ptr(jobs), n_jobs,
+                                         _stream(stream)), "sx_recompute_kv_realign")
 
 
 def sx_select_topk(dims: Dims, lay: Layout, q, q_index, sq_rows, sq_start, n_sq: int, lse,

@@ -454,6 +454,37 @@ sx_status sx_topk(const float* scores, const uint8_t* tok_class, const int32_t* 
                      const_cast<float*>(scores), ws, as_stream(stream));
 }
 
+sx_status sx_recompute_kv_realign(const sx_dims* dims, const sx_layout* lay, const void* x,
+                                  const int32_t* rows, int32_t n_rows, const void* w_qkv,
+                                  const sx_pages* kv, void* q_out, const sx_pages* rsrc,
+                                  const sx_pages* rdst, const sx_realign_job* jobs, int32_t n_jobs,
+                                  void* stream) {
+  const char* fn = "sx_recompute_kv_realign";
+  SX_TRY(check_dims(dims, fn));
+  SX_TRY(check_layout(lay, fn));
+  SX_TRY(check_pages(kv, fn, "kv"));
+  SX_TRY(check_pages(rsrc, fn, "rsrc"));
+  SX_TRY(check_pages(rdst, fn, "rdst"));
+  SX_REQUIRE(n_rows >= 0, SX_EINVAL, "%s: n_rows < 0", fn);
+  SX_REQUIRE(n_rows == 0 || (x && rows && w_qkv), SX_EINVAL, "%s: x/rows/w_qkv is NULL", fn);
+  SX_REQUIRE(n_jobs >= 0, SX_EINVAL, "%s: n_jobs < 0", fn);
+  SX_REQUIRE(n_jobs == 0 || jobs, SX_EINVAL, "%s: jobs is NULL", fn);
+  SX_REQUIRE(rdst->k != kv->k && rdst->v != kv->v && rdst->k != kv->v && rdst->v != kv->k, SX_EINVAL,
+             "%s: the realign destination must be another pool than kv", fn);
+  hipStream_t s = as_stream(stream);
+  if (debug_enabled() && (n_rows > 0 || n_jobs > 0)) {
+    DebugCheck dc(s, fn);
+    if (n_rows > 0) {
+      dc.layout(*lay, kv->n_pages, true);
+      dc.rows(rows, nullptr, n_rows, *lay);
+    }
+    if (n_jobs > 0) dc.jobs(jobs, n_jobs, rsrc->n_pages, rdst->n_pages, lay->rope_len);
+    SX_TRY(dc.finish());
+  }
+  return launch_recompute_realign(*dims, *lay, x, rows, n_rows, w_qkv, *kv, q_out, *rsrc, *rdst, jobs,
+                                  n_jobs, s);
+}
+
 sx_status sx_select_topk(const sx_dims* dims, const sx_layout* lay, const void* q,
                          const int32_t* q_index, const int32_t* sq_rows, const int32_t* sq_start,
                          int32_t n_sq, const float* lse, const sx_pages* kv,

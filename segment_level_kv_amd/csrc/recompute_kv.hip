@@ -12,6 +12,7 @@
 // running workgroups share W and X slices in their XCD's L2.  The epilogue
 // stages the fp32 tile in LDS, applies RoPE with the fp64-built table,
 // rounds to bf16 and writes 16-byte chunks (Q, K) or page columns (V).
+#include "realign_job.hpp"
 #include "sx_device.hpp"
 #include "sx_internal.hpp"
 
@@ -79,14 +80,36 @@ struct Gemm2Smem {
   };
 };
 
+// Realign jobs of another layer's pool carried by a projection launch: the
+// workgroups past the projection's tiles run them (launch_recompute_realign).
+struct SideRealign {
+  const uint16_t* ksrc;
+  const uint16_t* vsrc;
+  uint16_t* kdst;
+  uint16_t* vdst;
+  const sx_realign_job* jobs;
+  int n_src_pages, n_dst_pages, n_jobs;
+  int tile_blocks;             // blocks [0, tile_blocks) are projection tiles
+};
+
 template <int HPT>
 __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
     const uint16_t* __restrict__ x, int hidden, const int32_t* __restrict__ rows, int n_rows,
     const uint16_t* __restrict__ w, int head0, int n_tiles_m, int n_tiles_n, sx_layout lay,
     int n_pages, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
-    uint16_t* __restrict__ q_out, int hq, int hkv) {
+    uint16_t* __restrict__ q_out, int hq, int hkv, SideRealign side) {
   using Cfg = GemmCfg<HPT>;
   constexpr int NST2 = Cfg::NST, WROWS = Cfg::WROWS, MI = Cfg::MI, NCB = Cfg::NCB;
+  if ((int)blockIdx.x >= side.tile_blocks) {
+    // a realign worker, on a compute unit the projection's tiles leave free:
+    // an equal contiguous share of the side list, four pages at a time
+    const int w = blockIdx.x - side.tile_blocks, nw = gridDim.x - side.tile_blocks;
+    const int per = (side.n_jobs + nw - 1) / nw;
+    realign_job_run<4, GT>(side.jobs, min(w * per, side.n_jobs), min((w + 1) * per, side.n_jobs),
+                           side.ksrc, side.vsrc, side.kdst, side.vdst, side.n_src_pages,
+                           side.n_dst_pages, hkv, lay.rope_tab, lay.rope_len, threadIdx.x);
+    return;
+  }
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Gemm2Smem<HPT>& sm = *reinterpret_cast<Gemm2Smem<HPT>*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -513,9 +536,17 @@ int gemm_heads_per_tile(int mt, int n_heads) {
 
 }  // namespace
 
-sx_status launch_recompute(const sx_dims& dims, const sx_layout& lay, const void* x,
-                           const int32_t* rows, int n_rows, const void* w_qkv,
-                           const sx_pages& kv, void* q_out, hipStream_t stream) {
+namespace {
+
+// The projection of rows, with (side != nullptr) the realign jobs of another
+// pool in the same launch when the tiles leave at least kMinRealignWorkers
+// compute units free; *fused tells the caller whether they were.
+constexpr int kMinRealignWorkers = 16;
+sx_status launch_recompute_impl(const sx_dims& dims, const sx_layout& lay, const void* x,
+                                const int32_t* rows, int n_rows, const void* w_qkv,
+                                const sx_pages& kv, void* q_out, SideRealign* side, bool* fused,
+                                hipStream_t stream) {
+  *fused = false;
   if (n_rows == 0) return SX_OK;
   const int hq = dims.n_q_heads, hkv = dims.n_kv_heads;
   const int head0 = q_out ? 0 : hq;
@@ -536,11 +567,20 @@ sx_status launch_recompute(const sx_dims& dims, const sx_layout& lay, const void
     auto go = [&](auto kernel, int hpt, size_t smem) -> sx_status {
       const int nt = n_heads / hpt;
       const int grid = ((mt * nt + 7) / 8) * 8;
+      SideRealign none = {};
+      none.tile_blocks = grid;
+      int workers = 0;
+      if (side && side->n_jobs > 0 && kGemmCUs - grid >= kMinRealignWorkers) {
+        workers = kGemmCUs - grid;
+        side->tile_blocks = grid;
+        *fused = true;
+      }
       const sx_status st = allow_lds((const void*)kernel, smem, "sx_recompute_kv");
       if (st != SX_OK) return st;
-      kernel<<<grid, GT, smem, stream>>>(
+      kernel<<<grid + workers, GT, smem, stream>>>(
           (const uint16_t*)x, dims.hidden, rows, n_rows, (const uint16_t*)w_qkv, head0, mt, nt,
-          lay, kv.n_pages, (uint16_t*)kv.k, (uint16_t*)kv.v, (uint16_t*)q_out, hq, hkv);
+          lay, kv.n_pages, (uint16_t*)kv.k, (uint16_t*)kv.v, (uint16_t*)q_out, hq, hkv,
+          workers ? *side : none);
       return SX_OK;
     };
     const int hpt = gemm_heads_per_tile(mt, n_heads);
@@ -561,6 +601,43 @@ sx_status launch_recompute(const sx_dims& dims, const sx_layout& lay, const void
                                                      (float*)kv.k, (float*)kv.v, (float*)q_out, hq, hkv);
   }
   return check_launch("sx_recompute_kv");
+}
+
+}  // namespace
+
+sx_status launch_recompute(const sx_dims& dims, const sx_layout& lay, const void* x,
+                           const int32_t* rows, int n_rows, const void* w_qkv,
+                           const sx_pages& kv, void* q_out, hipStream_t stream) {
+  bool fused;
+  return launch_recompute_impl(dims, lay, x, rows, n_rows, w_qkv, kv, q_out, nullptr, &fused, stream);
+}
+
+// sx_recompute_kv of kv plus sx_rope_realign of rsrc -> rdst, which the
+// caller guarantees writes pages the projection does not touch.  One launch
+// when the projection's tiles leave compute units free (bf16, more than 64
+// rows, fewer than kGemmCUs - kMinRealignWorkers tiles): the realign jobs
+// run on those.  Otherwise the two launch one after the other.
+sx_status launch_recompute_realign(const sx_dims& dims, const sx_layout& lay, const void* x,
+                                   const int32_t* rows, int n_rows, const void* w_qkv,
+                                   const sx_pages& kv, void* q_out, const sx_pages& rsrc,
+                                   const sx_pages& rdst, const sx_realign_job* jobs, int n_jobs,
+                                   hipStream_t stream) {
+  SideRealign side = {};
+  if (dims.dtype == SX_BF16 && dims.head_dim == 128) {
+    side.ksrc = (const uint16_t*)rsrc.k;
+    side.vsrc = (const uint16_t*)rsrc.v;
+    side.kdst = (uint16_t*)rdst.k;
+    side.vdst = (uint16_t*)rdst.v;
+    side.jobs = jobs;
+    side.n_src_pages = rsrc.n_pages;
+    side.n_dst_pages = rdst.n_pages;
+    side.n_jobs = n_jobs;
+  }
+  bool fused = false;
+  const sx_status st = launch_recompute_impl(dims, lay, x, rows, n_rows, w_qkv, kv, q_out,
+                                             side.n_jobs > 0 ? &side : nullptr, &fused, stream);
+  if (st != SX_OK || fused) return st;
+  return launch_realign(dims, lay, rsrc, rdst, jobs, n_jobs, stream);
 }
 
 }  // namespace sx

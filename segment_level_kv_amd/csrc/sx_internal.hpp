@@ -33,6 +33,14 @@ sx_status launch_realign(const sx_dims& dims, const sx_layout& lay, const sx_pag
 sx_status launch_recompute(const sx_dims& dims, const sx_layout& lay, const void* x,
                            const int32_t* rows, int n_rows, const void* w_qkv,
                            const sx_pages& kv, void* q_out, hipStream_t stream);
+// launch_recompute of kv plus launch_realign of rsrc -> rdst (pages the
+// projection does not write), in one launch when the projection leaves
+// compute units free.
+sx_status launch_recompute_realign(const sx_dims& dims, const sx_layout& lay, const void* x,
+                                   const int32_t* rows, int n_rows, const void* w_qkv,
+                                   const sx_pages& kv, void* q_out, const sx_pages& rsrc,
+                                   const sx_pages& rdst, const sx_realign_job* jobs, int n_jobs,
+                                   hipStream_t stream);
 
 // Attention over the paged cache for rows grouped by request.
 //   rows == NULL: row m is packed token m (full prefill), row_start = seq_start.

@@ -181,14 +181,24 @@ class HybridStackRun:
         if self.keep_probe_cache:
             self.probe_k = self.req_pools[l].k.clone()
 
-    def sparse_prep(self, l: int, timer=None, realign: bool = True):
-        """Layer l's cache and queries: realign its reused runs, recompute A."""
+    def sparse_prep(self, l: int, timer=None, realign: bool = True, next_realign: bool = False):
+        """Layer l's cache and queries: realign its reused runs (unless done
+        already), recompute A.  next_realign: layer l+1's realign rides along
+        in the same launch (sx_recompute_kv_realign; the two write different
+        pools, and layer l+1's realign only has to finish before its own
+        recomputation)."""
         x, w, _ = self.inputs(l)
         pages = self.req_pools[l].struct()
         if realign:
             with _phase(timer, "realign"):
                 L.sx_rope_realign(self.cdims, self.lay.struct, self.src_pools[l].struct(), pages, self.jobs,
                                   len(self.jobs_h))
+        if next_realign:
+            with _phase(timer, "recompute_realign"):
+                L.sx_recompute_kv_realign(self.cdims, self.lay.struct, x, self.act_rows, self.n_act, w, pages,
+                                          self.q_act_buf[l % 2], self.src_pools[l + 1].struct(),
+                                          self.req_pools[l + 1].struct(), self.jobs, len(self.jobs_h))
+            return
         with _phase(timer, "recompute"):
             L.sx_recompute_kv(self.cdims, self.lay.struct, x, self.act_rows, self.n_act, w, pages,
                               self.q_act_buf[l % 2])
@@ -206,8 +216,8 @@ class HybridStackRun:
                                  self.n_act, self.req_pools[l].struct(), self.o_act[l], None,
                                  self.ws_attn)
 
-    def sparse_layer(self, l: int, timer=None, realign: bool = True):
-        self.sparse_prep(l, timer, realign)
+    def sparse_layer(self, l: int, timer=None, realign: bool = True, next_realign: bool = False):
+        self.sparse_prep(l, timer, realign, next_realign)
         self.sparse_attn(l, timer)
 
     def sparse_layers_pipelined(self, first: int, timer=None, first_realigned: bool = False):
@@ -284,17 +294,22 @@ class HybridStackRun:
             if pipelined:
                 self.sparse_layers_pipelined(self.t, timer)
             else:
-                for l in range(self.t, self.n_layers):
-                    self.sparse_layer(l, timer)
+                self.sparse_layers(self.t, timer)
         else:
             self.select_in_layer(0, timer)
             self.attn_plan(timer)
             if pipelined:
                 self.sparse_layers_pipelined(0, timer, first_realigned=True)
             else:
-                self.sparse_layer(0, timer, realign=False)
-                for l in range(1, self.n_layers):
-                    self.sparse_layer(l, timer)
+                self.sparse_layers(0, timer, first_realigned=True)
+
+    def sparse_layers(self, first: int, timer=None, first_realigned: bool = False):
+        """Sparse layers first..n-1 on one stream: each layer's recompute
+        launch also carries the next layer's realign (which then needs no
+        launch of its own); only layer `first` is realigned alone."""
+        for l in range(first, self.n_layers):
+            self.sparse_layer(l, timer, realign=(l == first and not first_realigned),
+                              next_realign=(l + 1 < self.n_layers))
 
 
 class _NoPhase:

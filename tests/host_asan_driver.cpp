@@ -36,6 +36,11 @@ sx_status launch_realign(const sx_dims&, const sx_layout&, const sx_pages&, cons
                          const sx_realign_job*, int, hipStream_t) { reached("launch_realign"); }
 sx_status launch_recompute(const sx_dims&, const sx_layout&, const void*, const int32_t*, int,
                            const void*, const sx_pages&, void*, hipStream_t) { reached("launch_recompute"); }
+sx_status launch_recompute_realign(const sx_dims&, const sx_layout&, const void*, const int32_t*, int,
+                                   const void*, const sx_pages&, void*, const sx_pages&, const sx_pages&,
+                                   const sx_realign_job*, int, hipStream_t) {
+  reached("launch_recompute_realign");
+}
 sx_status launch_attention(const sx_dims&, const sx_layout&, const void*, const int32_t*, const int32_t*,
                            const int32_t*, int, const sx_pages&, void*, float*, void*, hipStream_t) {
   reached("launch_attention");
@@ -254,6 +259,11 @@ static void device_entry_validation() {
   empty_bt.max_pages = 0;
   CHECK(sx_decode_attn_noalloc(&d, &empty_bt, fake_f, &pages, fake_f, nullptr, nullptr) == SX_EINVAL);
   CHECK(sx_rope_realign(&d, &lay, &pages, &pages, nullptr, 3, nullptr) == SX_EINVAL);
+  sx_pages other = {fake_i, fake_i, 4};
+  CHECK(sx_recompute_kv_realign(&d, &lay, fake_f, fake_i, 1, fake_f, &pages, nullptr, &other, &pages,
+                                nullptr, 1, nullptr) == SX_EINVAL);
+  CHECK(sx_recompute_kv_realign(&d, &lay, fake_f, fake_i, 1, fake_f, &pages, nullptr, &pages, &other,
+                                nullptr, 1, nullptr) == SX_EINVAL);
   CHECK(sx_select_topk(&d, &lay, fake_f, nullptr, fake_i, fake_i, 4, nullptr, &pages, nullptr, fake_i,
                        fake_i, nullptr, nullptr, ws, sizeof ws, nullptr) == SX_EINVAL);
   CHECK(sx_topk(nullptr, nullptr, fake_i, 1, 4, fake_i, fake_i, nullptr, 0, nullptr) == SX_EINVAL);

@@ -80,6 +80,15 @@ def test_validation_errors_launch_nothing():
     assert lib.sx_recompute_kv(C.byref(d), C.byref(bad_lay), FAKE, FAKE, 1, FAKE, C.byref(pages), None,
                                None) == L.SX_EINVAL
     assert lib.sx_topk(None, FAKE, FAKE, 1, 4, FAKE, FAKE, None, 0, None) == L.SX_EINVAL
+    # projection + next layer's realign: the realign destination must be another pool
+    other = L.Pages(0x2000, 0x3000, 4)
+    assert lib.sx_recompute_kv_realign(C.byref(d), C.byref(lay), FAKE, FAKE, 1, FAKE, C.byref(pages), None,
+                                       C.byref(other), C.byref(pages), FAKE, 1, None) == L.SX_EINVAL
+    assert "another pool" in L.last_error()
+    assert lib.sx_recompute_kv_realign(C.byref(d), C.byref(lay), FAKE, FAKE, 1, FAKE, C.byref(pages), None,
+                                       C.byref(other), C.byref(other), None, 1, None) == L.SX_EINVAL
+    assert lib.sx_recompute_kv_realign(C.byref(d), C.byref(lay), FAKE, FAKE, 1, FAKE, C.byref(pages), None,
+                                       C.byref(pages), C.byref(bad), FAKE, 1, None) == L.SX_EINVAL
     # plan / run halves of the sparse attention
     assert lib.sx_sparse_attn_plan(C.byref(d), C.byref(lay), None, FAKE, 4, FAKE, 1 << 20, None) == L.SX_EINVAL
     assert lib.sx_sparse_attn_plan(C.byref(d), C.byref(lay), FAKE, FAKE, 100, FAKE, 8, None) == L.SX_EWORKSPACE
@@ -112,6 +121,9 @@ def test_zero_sized_calls_are_noops():
     assert lib.sx_sparse_attn(C.byref(d), C.byref(lay), None, None, None, 0, C.byref(pages), None, None,
                               None, 0, None) == 0
     assert lib.sx_rope_realign(C.byref(d), C.byref(lay), C.byref(pages), C.byref(pages), None, 0, None) == 0
+    other = L.Pages(0x2000, 0x3000, 4)
+    assert lib.sx_recompute_kv_realign(C.byref(d), C.byref(lay), None, None, 0, None, C.byref(pages), None,
+                                       C.byref(pages), C.byref(other), None, 0, None) == 0
     assert lib.sx_sparse_attn_plan(C.byref(d), C.byref(lay), None, None, 0, None, 0, None) == 0
     assert lib.sx_sparse_attn_run(C.byref(d), C.byref(lay), None, None, 0, C.byref(pages), None, None,
                                   None, 0, None) == 0

@@ -244,6 +244,64 @@ def test_recompute_multi_head_tiles_sampled(n_rows):
         assert not np.any(changed_k & ~hit) and not np.any(changed_v & ~hit)
 
 
+@pytest.mark.parametrize("n_rows", [3379, 1500, 40, 6000])
+def test_recompute_with_next_realign_equals_two_calls(n_rows):
+    """sx_recompute_kv_realign (layer l's projection carrying layer l+1's
+    realign) gives the same bits as sx_recompute_kv followed by
+    sx_rope_realign: Q, the projection's pool and the realign destination
+    pool.  3,379 and 1,500 rows run the realign jobs on the compute units the
+    projection's tiles leave free (one launch); 40 rows (the few-rows kernel)
+    and 6,000 rows (more than one round of tiles) launch the two kernels one
+    after the other.  The jobs include full pages, partial slot ranges and
+    negative deltas."""
+    dims = SHAPES["llama"]
+    say(f"[recompute+realign] rows={n_rows}")
+    rng = np.random.default_rng(29)
+    seq = np.array([0, 4000, 6000], np.int32)
+    n_tok = int(seq[-1])
+    dt = LY.storage_dtype(dims.dtype)
+    x = torch.from_numpy(_store(synth._rmsnormed_gaussian(rng, n_tok, dims.hidden, dims.eps), dims)).to(dt).to(DEV)
+    w = torch.from_numpy(np.concatenate(synth._weights(rng, dims), axis=0)).to(dt).to(DEV)
+    rows = torch.from_numpy(np.sort(rng.choice(n_tok, size=n_rows, replace=False)).astype(np.int32)).to(DEV)
+    n_pages = 2 * 250 + 8
+    bt = rng.permutation(n_pages).astype(np.int32)[:500].reshape(2, 250)
+    rope = LY.rope_table(dims.theta, dims.head_dim, 6200, DEV)
+    lay = LY.DeviceLayout(seq, bt, rope, DEV)
+    cd = LY.make_dims(dims)
+    src = LY.PagePool.alloc(n_pages, dims, DEV, fill_guard=False)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(31)
+    src.k.copy_(torch.randn(src.k.shape, generator=g, device=DEV).to(dt))
+    src.v.copy_(torch.randn(src.v.shape, generator=g, device=DEV).to(dt))
+    jobs_h = []
+    for p in range(400):
+        d = int(rng.integers(-3000, 3000))
+        if p % 7 == 3:
+            s0, d0, n = int(rng.integers(0, 8)), int(rng.integers(0, 8)), int(rng.integers(1, 9))
+        else:
+            s0, d0, n = 0, 0, 16
+        jobs_h.append((int(rng.integers(0, n_pages)), int(bt.reshape(-1)[p]), s0, d0, n, d))
+    jobs = torch.tensor(jobs_h, dtype=torch.int32, device=DEV)
+
+    def fresh():
+        kv = LY.PagePool.alloc(n_pages, dims, DEV)
+        dst = LY.PagePool.alloc(n_pages, dims, DEV)
+        q = torch.full((n_rows, dims.n_q_heads, dims.head_dim), 7.0, dtype=dt, device=DEV)
+        return kv, dst, q
+
+    kv_a, dst_a, q_a = fresh()
+    L.sx_recompute_kv(cd, lay.struct, x, rows, n_rows, w, kv_a.struct(), q_a)
+    L.sx_rope_realign(cd, lay.struct, src.struct(), dst_a.struct(), jobs, len(jobs_h))
+    kv_b, dst_b, q_b = fresh()
+    L.sx_recompute_kv_realign(cd, lay.struct, x, rows, n_rows, w, kv_b.struct(), q_b, src.struct(),
+                              dst_b.struct(), jobs, len(jobs_h))
+    torch.cuda.synchronize()
+    for a, b, nm in [(q_a, q_b, "Q"), (kv_a.k, kv_b.k, "K pool"), (kv_a.v, kv_b.v, "V pool"),
+                     (dst_a.k, dst_b.k, "realigned K pool"), (dst_a.v, dst_b.v, "realigned V pool")]:
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), nm
+    assert not torch.equal(dst_b.k.view(torch.int16), LY.PagePool.alloc(n_pages, dims, DEV).k.view(torch.int16))
+
+
 # ---------------------------------------------------------------- attention --
 
 def _attn_inputs(dims, lens, seed):
