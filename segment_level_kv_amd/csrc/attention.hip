@@ -379,8 +379,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd(
   const int32_t* bt = lay.block_table + (size_t)req * lay.max_pages;
   const int kmax = k1 - 1;                 // last key of this item
   const int last_pi = max(min(kmax / kPage, lay.max_pages - 1), 0);
-  typedef __attribute__((address_space(1))) const void* gptr_t;
-  typedef __attribute__((address_space(3))) void* lptr_t;
   constexpr int NCP = 2;                   // copies of 1 KB per wave for K (and for V)
   const int wpart = w & 1;                 // which half of its page a wave copies
   uint32_t koff[NCP], voff[NCP];           // byte offsets inside a page-head
@@ -416,7 +414,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd(
     unsigned char* kst = reinterpret_cast<unsigned char*>(&st[s].k[8 * wu][0]);
 #pragma unroll
     for (int i = 0; i < NCP; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(kp + koff[i]), (lptr_t)(kst + i * 1024), 16, 0, 0);
+      copy16_to_lds(kp + koff[i], kst + i * 1024);
   };
   auto issue_v = [&](int pg, int s) __attribute__((always_inline)) {
     if (!WITH_O) return;
@@ -425,7 +423,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd(
     unsigned char* vst = reinterpret_cast<unsigned char*>(&st[s].v[wpage][64 * (wu & 1)][0]);
 #pragma unroll
     for (int i = 0; i < NCP; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(vp + voff[i]), (lptr_t)(vst + i * 1024), 16, 0, 0);
+      copy16_to_lds(vp + voff[i], vst + i * 1024);
   };
   auto issue_stage = [&](int pg, int s) __attribute__((always_inline)) {
     issue_k(pg, s);

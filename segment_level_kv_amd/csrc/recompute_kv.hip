@@ -12,6 +12,8 @@
 // running workgroups share W and X slices in their XCD's L2.  The epilogue
 // stages the fp32 tile in LDS, applies RoPE with the fp64-built table,
 // rounds to bf16 and writes 16-byte chunks (Q, K) or page columns (V).
+#include <type_traits>
+
 #include "realign_job.hpp"
 #include "sx_device.hpp"
 #include "sx_internal.hpp"
@@ -137,8 +139,6 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
   // lane loads chunk (L % 8) ^ (R & 7).  Rows past n_rows (or with a token
   // outside the sequence) read row 0 of x: finite data whose results are
   // never stored.
-  typedef __attribute__((address_space(1))) const void* gptr_t;
-  typedef __attribute__((address_space(3))) void* lptr_t;
   size_t a_off[NCA];                         // byte offsets of this lane's chunks at k = 0
   uint32_t b_off[NCB];
 #pragma unroll
@@ -167,10 +167,10 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
     unsigned char* bs = reinterpret_cast<unsigned char*>(&sm.st[slot].b[8 * NCB * wu][0]);
 #pragma unroll
     for (int i = 0; i < NCA; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(xb + a_off[i] + kb), (lptr_t)(as + i * 1024), 16, 0, 0);
+      copy16_to_lds(xb + a_off[i] + kb, as + i * 1024);
 #pragma unroll
     for (int i = 0; i < NCB; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(wb + b_off[i] + kb), (lptr_t)(bs + i * 1024), 16, 0, 0);
+      copy16_to_lds(wb + b_off[i] + kb, bs + i * 1024);
   };
 
   constexpr int NJ = Cfg::NJ, NBUF = Cfg::NBUF;
@@ -258,85 +258,107 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
   }
 
   // ---- epilogue, one head at a time: its fp32 columns -> LDS -------------
-  for (int h = 0; h < HPT; ++h) {
-  if (h > 0) __syncthreads();                  // every thread done with the previous head
+  // Each wave column (wn) runs its own copy of this code, so which
+  // accumulators a wave still holds is known at compile time and a head's
+  // accumulators are dead once staged.  With three heads the middle one,
+  // split between the two wave columns, goes first: no wave then holds more
+  // than two of its three heads' accumulators while the RoPE table entries
+  // are in registers (in head order a wave held all of them and spilled).
+  // Every copy passes the same barriers in the same order.
+  auto store_head = [&](const int head) __attribute__((always_inline)) {
+    if (head < hq + hkv) {
+      // Q or K head: rotate-half pairs (e, e+64), 8 pairs per unit; a thread
+      // takes 8 units (rows tid/8 + 32 k), first loading all their RoPE table
+      // entries, then rotating and storing.
+      const bool is_q = head < hq;
+      const int g = head - hq;
+      constexpr int kUnits = BM2 * 8 / GT;
+      const int c = tid & 7;
+      f32x4 tabv[kUnits][4];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int col = wn * Cfg::WCOLS + j * 32;  // first tile column of this 32-column block
-    if (col / BN != h) continue;               // wave-uniform
+      for (int k = 0; k < kUnits; ++k) {
+        const int m = (tid >> 3) + (GT / 8) * k;
+        const f32x4* tab = reinterpret_cast<const f32x4*>(lay.rope_tab + (size_t)ep.row_pos[m] * 128 + c * 16);
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * WROWS + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        ep.c[r][col % BN + (lane & 31)] = acc[i][j][v];
+        for (int i = 0; i < 4; ++i) tabv[k][i] = tab[i];
       }
-  }
-  __syncthreads();
-  const int head = head1 + h;
-
-  if (head < hq + hkv) {
-    // Q or K head: rotate-half pairs (e, e+64), 8 pairs per unit; a thread
-    // takes 8 units (rows tid/8 + 32 k), first loading all their RoPE table
-    // entries, then rotating and storing.
-    const bool is_q = head < hq;
-    const int g = head - hq;
-    constexpr int kUnits = BM2 * 8 / GT;
-    const int c = tid & 7;
-    f32x4 tabv[kUnits][4];
 #pragma unroll
-    for (int k = 0; k < kUnits; ++k) {
-      const int m = (tid >> 3) + (GT / 8) * k;
-      const f32x4* tab = reinterpret_cast<const f32x4*>(lay.rope_tab + (size_t)ep.row_pos[m] * 128 + c * 16);
+      for (int k = 0; k < kUnits; ++k) {
+        const int m = (tid >> 3) + (GT / 8) * k;
+        uint16_t* dst = nullptr;
+        if (is_q) {
+          if (q_out && ep.row_ok[m]) dst = q_out + ((size_t)(m0 + m) * hq + head) * 128;
+        } else {
+          const int page = ep.row_page[m];
+          if (page >= 0) dst = kpool + (((size_t)page * hkv + g) * kPage + ep.row_slot[m]) * 128;
+        }
+        float olo[8], ohi[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tabv[k][i] = tab[i];
-    }
+        for (int e = 0; e < 8; ++e) {
+          const float lo = ep.c[m][c * 8 + e], hi = ep.c[m][64 + c * 8 + e];
+          const float cs = tabv[k][e >> 1][2 * (e & 1)], sn = tabv[k][e >> 1][2 * (e & 1) + 1];
+          olo[e] = lo * cs - hi * sn;
+          ohi[e] = lo * sn + hi * cs;
+        }
+        u32x4 plo, phi;
 #pragma unroll
-    for (int k = 0; k < kUnits; ++k) {
-      const int m = (tid >> 3) + (GT / 8) * k;
-      uint16_t* dst = nullptr;
-      if (is_q) {
-        if (q_out && ep.row_ok[m]) dst = q_out + ((size_t)(m0 + m) * hq + head) * 128;
-      } else {
-        const int page = ep.row_page[m];
-        if (page >= 0) dst = kpool + (((size_t)page * hkv + g) * kPage + ep.row_slot[m]) * 128;
+        for (int e = 0; e < 4; ++e) {
+          plo[e] = pack_bf2(olo[2 * e], olo[2 * e + 1]);
+          phi[e] = pack_bf2(ohi[2 * e], ohi[2 * e + 1]);
+        }
+        if (dst) {
+          *reinterpret_cast<u32x4*>(dst + c * 8) = plo;
+          *reinterpret_cast<u32x4*>(dst + 64 + c * 8) = phi;
+        }
       }
-      float olo[8], ohi[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float lo = ep.c[m][c * 8 + e], hi = ep.c[m][64 + c * 8 + e];
-        const float cs = tabv[k][e >> 1][2 * (e & 1)], sn = tabv[k][e >> 1][2 * (e & 1) + 1];
-        olo[e] = lo * cs - hi * sn;
-        ohi[e] = lo * sn + hi * cs;
-      }
-      u32x4 plo, phi;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        plo[e] = pack_bf2(olo[2 * e], olo[2 * e + 1]);
-        phi[e] = pack_bf2(ohi[2 * e], ohi[2 * e + 1]);
-      }
-      if (dst) {
-        *reinterpret_cast<u32x4*>(dst + c * 8) = plo;
-        *reinterpret_cast<u32x4*>(dst + 64 + c * 8) = phi;
-      }
-    }
-  } else {
-    // V head: page layout [d][slot]; thread tid takes output row tid % 256
-    // and half of its 128 d (2-byte stores 32 bytes apart in its page).
-    const int g = head - hq - hkv;
-    constexpr int kDim = 128 * BM2 / GT;     // head dimensions per thread
-    const int row = tid % BM2, e0 = (tid / BM2) * kDim;
-    const int page = ep.row_page[row];
-    if (page >= 0) {
-      uint16_t* base = vpool + ((size_t)page * hkv + g) * 128 * kPage + ep.row_slot[row];
+    } else {
+      // V head: page layout [d][slot]; thread tid takes output row tid % 256
+      // and half of its 128 d (2-byte stores 32 bytes apart in its page).
+      const int g = head - hq - hkv;
+      constexpr int kDim = 128 * BM2 / GT;     // head dimensions per thread
+      const int row = tid % BM2, e0 = (tid / BM2) * kDim;
+      const int page = ep.row_page[row];
+      if (page >= 0) {
+        uint16_t* base = vpool + ((size_t)page * hkv + g) * 128 * kPage + ep.row_slot[row];
 #pragma unroll 4
-      for (int e = e0; e < e0 + kDim; e += 4) {
-        const f32x4 c4 = *reinterpret_cast<const f32x4*>(&ep.c[row][e]);
+        for (int e = e0; e < e0 + kDim; e += 4) {
+          const f32x4 c4 = *reinterpret_cast<const f32x4*>(&ep.c[row][e]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) base[(e + i) * kPage] = f2bf(c4[i]);
+          for (int i = 0; i < 4; ++i) base[(e + i) * kPage] = f2bf(c4[i]);
+        }
       }
     }
-  }
+  };
+  auto epilogue = [&](auto wn_tag) __attribute__((always_inline)) {
+    constexpr int WN = decltype(wn_tag)::value;
+#pragma unroll
+    for (int hi = 0; hi < HPT; ++hi) {
+      const int h = HPT == 3 ? (hi == 0 ? 1 : hi == 1 ? 0 : 2) : hi;
+      if (hi > 0) __syncthreads();             // every thread done with the previous head
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int col = WN * Cfg::WCOLS + j * 32;   // first tile column of this 32-column block
+        if (col / BN != h) continue;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = wm * WROWS + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            ep.c[r][col % BN + (lane & 31)] = acc[i][j][v];
+          }
+      }
+      __syncthreads();
+      store_head(head1 + h);
+    }
+  };
+  static_assert(Cfg::WGN == 2 || Cfg::WGN == 4, "wave columns");
+  if (wn == 0) {
+    epilogue(std::integral_constant<int, 0>{});
+  } else if (wn == 1) {
+    epilogue(std::integral_constant<int, 1>{});
+  } else if constexpr (Cfg::WGN == 4) {
+    if (wn == 2) epilogue(std::integral_constant<int, 2>{});
+    else epilogue(std::integral_constant<int, 3>{});
   }
 }
 

@@ -47,6 +47,23 @@ __device__ __forceinline__ f32x2_t unpack_h2(uint32_t v) {
   return __builtin_convertvector(__builtin_bit_cast(f16x2_t, v), f32x2_t);
 }
 
+// One 16-byte chunk per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane L writes bytes [16 L, 16 L + 16) after
+// the wave's LDS base `lds` (wave-uniform, passed in M0).  It is issued as
+// inline asm rather than through the compiler builtin: the compiler counts
+// the builtin as a FLAT access that may write LDS, and while one is
+// pending its wait-count pass can only wait for an LDS read with
+// lgkmcnt(0), which drains every LDS read in flight before the first
+// operand is used.  The asm has no register result.  The compiler does not
+// count these loads; since loads complete in issue order, that only makes
+// its own vmcnt waits stricter.  Callers order the LDS writes themselves,
+// with vmcnt waits and barriers before any wave reads the bytes.
+__device__ __forceinline__ void copy16_to_lds(const void* gsrc, const void* lds) {
+  typedef __attribute__((address_space(3))) const void* lds_ptr_t;
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
+}
+
 // Request owning packed token `tok` (seq_start ascending, n_req+1 entries).
 // Returns -1 if tok is outside [seq_start[0], seq_start[n_req]).
 __device__ __forceinline__ int find_request(const int32_t* __restrict__ seq_start, int n_req, int tok) {
