@@ -26,8 +26,9 @@ constexpr int BN = 128, BK = 64;
 constexpr int LDC = BN + 4;          // padded fp32 row of the staged output tile
 constexpr int GROUP_M = 4;
 
-// bf16 GEMM, 256-row output tiles of one or two heads.  K-steps of 64 go
-// global -> LDS directly (global_load_lds_dwordx4) into a ring of stages;
+// bf16 GEMM, 256-row output tiles of one, two or three heads.  K-steps of
+// 64 go global -> LDS directly (global_load_lds_dwordx4, copy16_to_lds) into
+// a ring of stages;
 // each 128-byte LDS row keeps its 16-byte chunk c at position c ^ (row & 7),
 // so the rows an MFMA operand read touches spread over the banks.  Eight
 // waves, two per SIMD, each of 64 columns and 64 or 128 rows in 32 x 32
