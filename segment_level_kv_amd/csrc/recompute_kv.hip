@@ -44,8 +44,8 @@ constexpr int NCA = BM2 * BK * 2 / 1024 / GW;   // 1 KB stage copies per wave: A
 // of 3, waves 4 x 2 of 64 x 64.  HPT = 2 (256 x 256 tiles, 1.5x the flops
 // per staged byte): 64 KB stages in a ring of 2, waves 2 x 4 of 128 x 64.
 // HPT = 3 (256 x 384 tiles, 1.8x): 80 KB stages in a ring of 2 (the whole
-// LDS), waves 4 x 2 of 64 x 192 (192 accumulator registers per lane, so the
-// next k-slice's operands are not read ahead).
+// LDS), waves 4 x 2 of 64 x 192 (192 accumulator registers per lane, so only
+// the next B fragment is read ahead, not the next k-slice's operands).
 template <int HPT>
 struct GemmCfg {
   static constexpr int BNT = BN * HPT;              // output columns per tile
@@ -220,9 +220,16 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
       }
     } else {
-      // one operand buffer: the A fragments of a slice, then each B fragment
-      // just before its MFMAs (few operand registers live next to 192
-      // accumulators)
+      // one operand buffer (few operand registers live next to 192
+      // accumulators): the A fragments of a slice, and the B fragments one
+      // MFMA group ahead, so each B read has the previous group's MFMAs to
+      // land behind (3% faster at 3,379 rows than reading each just before
+      // its MFMAs)
+      auto read_b = [&](int ks, int j) __attribute__((always_inline)) {
+        const int R = wn * Cfg::WCOLS + j * 32 + lr;
+        return *reinterpret_cast<const bf16x8*>(&S.b[R][((2 * ks + lh) ^ (R & 7)) * 8]);
+      };
+      bf16x8 b_next = read_b(0, 0);
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
         const int ch = 2 * ks + lh;
@@ -233,8 +240,9 @@ __global__ __launch_bounds__(GT, 1) void qkv_gemm256_bf16(
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const int R = wn * Cfg::WCOLS + j * 32 + lr;
-          const bf16x8 bj = *reinterpret_cast<const bf16x8*>(&S.b[R][(ch ^ (R & 7)) * 8]);
+          const bf16x8 bj = b_next;
+          if (j + 1 < NJ) b_next = read_b(ks, j + 1);
+          else if (ks + 1 < BK / 16) b_next = read_b(ks + 1, 0);
 #pragma unroll
           for (int i = 0; i < MI; ++i)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bj, acc[i][j], 0, 0, 0);
