@@ -304,16 +304,20 @@ __device__ __forceinline__ float half_sum(float x) {
 }
 
 // s_waitcnt with at most VM vector-memory operations of this wave still in
-// flight and no LDS / scalar operation pending, then the workgroup barrier.
-// The stage copies (global_load_lds) write LDS asynchronously and are
-// tracked only by vmcnt, which the barrier itself does not wait for.
+// flight, then the workgroup barrier.  The stage copies (global_load_lds)
+// write LDS asynchronously and are tracked only by vmcnt, which the barrier
+// itself does not wait for.  LDS reads may still be in flight: the ones a
+// wave issues just before the barrier load the next step's operands from
+// stages that stay resident, and every read of the slot the copies after
+// the barrier overwrite was consumed by an MFMA, hence complete, before the
+// wave reached it (waiting for them here as well cost 2% of the loop).
 // Written as one asm block: the compiler's own fence for a barrier would
 // otherwise be merged into the wait and turn it into vmcnt(0).  The memory
 // clobber keeps LDS accesses on their side of the barrier.
 template <int VM>
 __device__ __forceinline__ void vm_wait_barrier() {
   static_assert(VM >= 0 && VM < 64, "vmcnt field");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
 // One workgroup: 8 waves of 32 (row, head) pairs each, two waves per SIMD.
@@ -443,12 +447,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd(
       vs[(j * 128 + d) * kPage + half * 8 + (kk & 7)] = 0;
     }
   };
-  // The barrier asm above waits for every LDS and scalar load (lgkmcnt(0)),
-  // but the compiler does not read asm: this real s_waitcnt lgkmcnt(0) (no
-  // cost right after it) tells its wait insertion that the scalar page-id
-  // loads are done.  With a scalar load pending, scalar results may return
-  // out of order with LDS reads, so every wait for an LDS read would have to
-  // be lgkmcnt(0) and drain all of the step's LDS reads in flight.
+  // After the stage barrier: waits for the scalar page-id load (and the LDS
+  // reads still in flight, which lgkmcnt counts with it), as a real
+  // s_waitcnt the compiler's wait insertion sees.  With a scalar load
+  // pending, scalar results may return out of order with LDS reads, so
+  // every later wait for an LDS read would have to be lgkmcnt(0) and drain
+  // all of the step's LDS reads in flight.
   auto lgkm_settled = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63, expcnt 7, lgkmcnt 0 (gfx9 encoding)
   };
