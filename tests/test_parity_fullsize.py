@@ -102,3 +102,109 @@ def test_agent_batch_full_size_sampled():
 
 def test_qwen128k_layer_full_size_sampled():
     _check_full_size(synth.qwen128k_case(), 24)
+
+
+
+def _rag32k_attention_run(q_zero: bool, v_const: bool, seed: int):
+    """The sparse attention alone at the full rag32k shape, in the launch
+    configuration the bench times (the work list built once with
+    sx_sparse_attn_plan, then sx_sparse_attn_run, twice): 31,488 tokens in
+    shuffled pages, 3,379 active rows (the 256 new tokens and 3,123 reused
+    positions drawn uniformly), random bf16 K; Q random or zero, V random or
+    a constant vector per kv head.  Returns the host inputs and the output,
+    after checking that the two runs gave the same bits."""
+    from segment_level_kv_amd import _lib as L
+    from segment_level_kv_amd import layer as LY
+    dims = synth.Dims(hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, theta=5e5, dtype="bf16")
+    T, n_new, n_sel = 31488, 256, 3123
+    rng = np.random.default_rng(seed)
+    n_pages = (T + 15) // 16 + 8
+    perm = rng.permutation(n_pages).astype(np.int32)
+    bt = perm[:(T + 15) // 16][None, :].copy()
+    rows = np.union1d(rng.choice(T - n_new, size=n_sel, replace=False),
+                      np.arange(T - n_new, T)).astype(np.int32)
+    n_rows = len(rows)
+    c = synth.to_storage(rng.uniform(-1.0, 1.0, (dims.n_kv_heads, dims.head_dim)), "bf16")
+    say(f"[fullsize] attention alone: T={T}, {n_rows} active rows, Q {'zero' if q_zero else 'random'}, "
+        f"V {'constant' if v_const else 'random'}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    k = torch.randn((n_pages, dims.n_kv_heads, 16, dims.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+    if v_const:
+        v = torch.from_numpy(c).to(torch.bfloat16).to("cuda")[None, :, :, None].expand(
+            n_pages, dims.n_kv_heads, dims.head_dim, 16).contiguous()
+    else:
+        v = torch.randn((n_pages, dims.n_kv_heads, dims.head_dim, 16), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((n_rows, dims.n_q_heads, dims.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+    if q_zero:
+        q.zero_()
+    pool = LY.PagePool(k, v)
+    lay = LY.DeviceLayout(np.array([0, T], np.int32), bt, LY.rope_table(dims.theta, dims.head_dim, 16, "cuda"),
+                          "cuda")
+    cd = LY.make_dims(dims)
+    rows_t = torch.from_numpy(rows).to("cuda")
+    starts = torch.tensor([0, n_rows], dtype=torch.int32, device="cuda")
+    ws = LY.workspace(L.SX_OP_SPARSE_ATTN, cd, T, n_rows, 1, "cuda")
+    L.sx_sparse_attn_plan(cd, lay.struct, rows_t, starts, n_rows, ws)
+    outs = []
+    for _ in range(2):
+        o = torch.empty((n_rows, dims.n_q_heads * dims.head_dim), dtype=torch.bfloat16, device="cuda")
+        L.sx_sparse_attn_run(cd, lay.struct, q, rows_t, n_rows, pool.struct(), o, None, ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), "repeated run differs"
+    og = outs[0].float().cpu().double().numpy().reshape(n_rows, dims.n_q_heads, dims.head_dim)
+    assert np.all(np.isfinite(og))
+    return dims, bt, rows, c, v, og
+
+
+def test_rag32k_sparse_attention_every_output_constant_v():
+    """Pin P9 at the full rag32k attention shape, every output element: V
+    equal to a constant vector c_g for every key of kv head g.  The softmax
+    weights of a row sum to one, so every output row of a query head of group
+    g is c_g (the paper's §3.2: Sparse-Q rows attend to all available keys;
+    the value is the weighted mean of V).  Bound: P enters P V rounded to
+    bf16 (relative error at most half a bf16 step, 2^-8, per weight) while
+    the row sum uses the fp32 weights, and O is stored in bf16 (another
+    2^-8); the fp32 sums over up to 31,488 keys add about 1e-5.  So
+    |O - c| <= (2^-7 + 1e-4) |c|, below the 1e-2 contract for |c| <= 1."""
+    dims, bt, rows, c, v, og = _rag32k_attention_run(q_zero=False, v_const=True, seed=2024)
+    G = dims.n_q_heads // dims.n_kv_heads
+    ref = np.repeat(c.astype(np.float64), G, axis=0)[None, :, :]
+    err = np.abs(og - ref)
+    tol = (2.0 ** -7 + 1e-4) * np.abs(ref) + 1e-6
+    bad = err > tol
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} outputs outside (2^-7 + 1e-4) |c|; max err "
+                           f"{err.max():.3g} at {np.unravel_index(err.argmax(), err.shape)}")
+    assert err.max() <= 1e-2
+    say(f"[fullsize]   {og.size} outputs, max |O - c| = {err.max():.3g}")
+
+
+def test_rag32k_sparse_attention_every_output_uniform_softmax():
+    """Pin P8's attention half at the full rag32k shape, every output
+    element: with Q = 0 every logit is 0, the causal softmax of the row at
+    position p is uniform over keys 0..p, and its output is the mean of
+    V[0..p] (the paper's §3.2: each Sparse-Q row attends to all keys up to
+    its own position).  The reference is the fp64 prefix mean of the V
+    values read through the block table, for every active row and head; it
+    checks the causal limit of every row and the page mapping of every key.
+    Bound: the weights are exactly 1 in bf16 and the row sums exact in fp32;
+    the fp32 sums of bf16 values add well under 1e-4 of absolute error to a
+    mean, and O is stored in bf16 (half a step, 2^-8 |r|)."""
+    dims, bt, rows, c, v, og = _rag32k_attention_run(q_zero=True, v_const=False, seed=77)
+    G = dims.n_q_heads // dims.n_kv_heads
+    T = int(rows[-1]) + 1
+    say("[fullsize]   prefix means on the host")
+    vh = v.float().cpu().double().numpy()                     # [pages][Hkv][d][16]
+    tok = np.arange(T)
+    v_log = vh[bt[0][tok // 16], :, :, tok % 16]              # [T][Hkv][d]
+    csum = np.cumsum(v_log, axis=0)
+    ref = csum[rows] / (rows + 1.0)[:, None, None]            # [rows][Hkv][d]
+    ref = np.repeat(ref, G, axis=1)
+    err = np.abs(og - ref)
+    tol = 2.0 ** -8 * np.abs(ref) + 1e-4
+    bad = err > tol
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} outputs outside 2^-8 |r| + 1e-4; max err "
+                           f"{err.max():.3g} at {np.unravel_index(err.argmax(), err.shape)}")
+    assert err.max() <= 1e-2
+    say(f"[fullsize]   {og.size} outputs, max |O - mean V| = {err.max():.3g}")
