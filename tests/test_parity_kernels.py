@@ -183,14 +183,13 @@ def test_recompute_parity_and_scatter(shape, n_rows):
 
 
 @pytest.mark.parametrize("n_rows", [5200, 3379])
-def test_recompute_multi_head_tiles_sampled(n_rows):
+def test_recompute_multi_head_tiles_every_row(n_rows):
     """Row counts whose launch takes multi-head tiles: 5,200 of 6,000 tokens
     in Llama shapes take 256 x 256 tiles (two heads), with Q (48 heads) and
     K/V only (16 heads); 3,379 rows (the rag32k active-set size) take
     256 x 384 tiles (three heads) with Q, one-head tiles K/V only.  The
-    oracle projects 320 sampled rows, spread over every row tile and
-    including the last, partial one; every head of every tile is compared,
-    and exactly the listed rows' slots are written."""
+    oracle projects every row (the last row tile is partial); every head of
+    every row is compared, and exactly the listed rows' slots are written."""
     dims = SHAPES["llama"]
     say(f"[recompute] multi-head tiles: rows={n_rows}")
     rng = np.random.default_rng(23)
@@ -213,9 +212,7 @@ def test_recompute_multi_head_tiles_sampled(n_rows):
     rt = torch.from_numpy(rows).to(DEV)
     req = (rows >= 4000).astype(int)
     idx = rows - seq[req]
-    sample = np.unique(np.concatenate([np.arange(0, n_rows, 17), np.arange(n_rows - 64, n_rows)]))
-    sample = sample[np.linspace(0, len(sample) - 1, 320).astype(int)]
-    sample = np.union1d(sample, np.arange(n_rows - 16, n_rows))
+    sample = np.arange(n_rows)
     s_rows = rows[sample]
     qr, kr, vr = oracle.project_rows(x[s_rows], case_w[0], case_w[1], case_w[2],
                                      idx[sample] + pos_off[req[sample]], dims.theta,
